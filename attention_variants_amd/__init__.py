@@ -1,0 +1,220 @@
+"""MI355X-native fused attention variants -- Python binding of ``libattnvar.so``.
+
+Thin ctypes layer over the C ABI declared in ``include/attnvar.h``: it checks
+tensor dtypes, devices and shapes, allocates outputs with ``torch.empty`` and
+passes raw device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, every entry point raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnvar.so")
+
+SCORE_MODS = {"none": 0, "alibi": 1, "softcap": 2}
+MASKS = {"none": 0, "causal": 1, "sliding_window": 2, "prefix_lm": 3, "document": 4}
+
+AV_OK = 0
+STATUS = {
+    0: "AV_OK",
+    -1: "AV_ERR_NULL",
+    -2: "AV_ERR_SHAPE",
+    -3: "AV_ERR_UNSUPPORTED",
+    -4: "AV_ERR_ALIGN",
+    -5: "AV_ERR_WORKSPACE",
+    -6: "AV_ERR_HIP",
+    -7: "AV_ERR_PARAM",
+    -8: "AV_ERR_TOO_LARGE",
+}
+
+# Names the header declares; tests check that the library exports each one.
+EXPORTED = (
+    "attn_fwd",
+    "diff_attn_fwd",
+    "evoformer_workspace_bytes",
+    "evoformer_gated_attn_fwd",
+    "av_status_string",
+    "av_abi_version",
+)
+
+
+class AvVariant(ctypes.Structure):
+    """Mirror of ``av_variant`` in ``include/attnvar.h``."""
+
+    _fields_ = [
+        ("score_mod", ctypes.c_int32),
+        ("mask", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("alibi_max_bias", ctypes.c_float),
+        ("window", ctypes.c_int32),
+        ("prefix_len", ctypes.c_int32),
+        ("doc_id", ctypes.c_void_p),
+        ("kv_group", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+def load_library(path: str | None = None):
+    """Load the in-tree ``libattnvar.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"attention_variants_amd: HIP library missing at {p}; build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(p)
+    lib.attn_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_fwd.restype = _i
+    lib.diff_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp]
+    lib.diff_attn_fwd.restype = _i
+    lib.evoformer_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    lib.evoformer_workspace_bytes.restype = ctypes.c_size_t
+    lib.evoformer_gated_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                             _i, _i, _i, _i, _i, _f, _vp]
+    lib.evoformer_gated_attn_fwd.restype = _i
+    lib.av_status_string.argtypes = [_i]
+    lib.av_status_string.restype = ctypes.c_char_p
+    lib.av_abi_version.argtypes = []
+    lib.av_abi_version.restype = _i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(rc: int) -> str:
+    return load_library().av_status_string(rc).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != AV_OK:
+        raise RuntimeError(f"{what}: {status_string(rc)}")
+
+
+def _stream_ptr(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alibi_max_bias=8.0,
+                 window=256, prefix_len=0, doc_id=None, kv_group=0) -> AvVariant:
+    if score_mod not in SCORE_MODS:
+        raise ValueError(f"unknown score_mod {score_mod!r}")
+    if mask not in MASKS:
+        raise ValueError(f"unknown mask {mask!r}")
+    return AvVariant(SCORE_MODS[score_mod], MASKS[mask], float(scale or 0.0), float(softcap),
+                     float(alibi_max_bias), int(window), int(prefix_len),
+                     None if doc_id is None else int(doc_id.data_ptr()), int(kv_group))
+
+
+def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0, alibi_max_bias=8.0,
+             window=256, prefix_len=0, doc_id=None, kv_group=0, return_lse=False, out=None, lse=None):
+    """Fused attention forward.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] bf16 -> out [B,Hq,Sq,D] (bf16).
+
+    With ``return_lse`` also returns the fp32 natural-log sum-exp per row.
+    """
+    import torch
+
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if doc_id is not None:
+        _need(doc_id, "doc_id", torch.int32, 2)
+        if tuple(doc_id.shape) != (B, Sq):
+            raise ValueError("doc_id must be [B, S]")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
+                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group)
+    rc = lib.attn_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      None if lse is None else lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
+    _check(rc, "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def diff_attn_fwd(q, k, v, *, lam=0.8, scale=0.0, causal=True, out=None):
+    """Differential attention.  q, k [B,H,S,2*Dh], v [B,H,S,Dv] bf16 -> out [B,H,S,Dv]."""
+    import torch
+
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H, S, D2 = q.shape
+    if tuple(k.shape) != (B, H, S, D2) or v.shape[:3] != (B, H, S) or D2 % 2:
+        raise ValueError("shape mismatch")
+    Dv = v.shape[3]
+    if out is None:
+        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=q.device)
+    rc = lib.diff_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, S, D2 // 2, Dv,
+                           float(lam), float(scale or 0.0), int(bool(causal)), _stream_ptr(q.device))
+    _check(rc, "diff_attn_fwd")
+    return out
+
+
+def evoformer_workspace_bytes(Ns, Nr, H, dh) -> int:
+    return int(load_library().evoformer_workspace_bytes(Ns, Nr, H, dh))
+
+
+def evoformer_gated_attn_fwd(m, wq, wk, wv, wg, bias, *, H, dh, scale=0.0, workspace=None, out=None):
+    """Evoformer row-wise gated self-attention with pair bias.
+
+    m [Ns,Nr,Cm], w* [Cm,H*dh], bias [H,Nr,Nr] bf16 -> out [Ns,Nr,H*dh] bf16.
+    ``workspace`` (uint8 device tensor) is allocated when not given.
+    """
+    import torch
+
+    lib = load_library()
+    _need(m, "m", torch.bfloat16, 3)
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
+        _need(t, n, torch.bfloat16, 2)
+    _need(bias, "bias", torch.bfloat16, 3)
+    Ns, Nr, Cm = m.shape
+    for t in (wq, wk, wv, wg):
+        if tuple(t.shape) != (Cm, H * dh):
+            raise ValueError("projection weights must be [Cm, H*dh]")
+    if tuple(bias.shape) != (H, Nr, Nr):
+        raise ValueError("bias must be [H, Nr, Nr]")
+    need = evoformer_workspace_bytes(Ns, Nr, H, dh)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=m.device)
+    if out is None:
+        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=m.device)
+    rc = lib.evoformer_gated_attn_fwd(m.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wg.data_ptr(),
+                                      bias.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      Ns, Nr, Cm, H, dh, float(scale or 0.0), _stream_ptr(m.device))
+    _check(rc, "evoformer_gated_attn_fwd")
+    return out

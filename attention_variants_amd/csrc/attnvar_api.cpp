@@ -1,0 +1,169 @@
+// C ABI of the attention-variant library: host-side validation, derived
+// launch parameters, dispatch.  Nothing here touches the GPU until every
+// argument has been checked, so every error path is testable without one.
+
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attnvar.h"
+#include "av_kernels.hpp"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+constexpr uint64_t kMaxSliceBytes = (1ull << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? AV_OK : AV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int av_abi_version(void) { return AV_ABI_VERSION; }
+
+const char* av_status_string(int status) {
+  switch (status) {
+    case AV_OK: return "AV_OK: success";
+    case AV_ERR_NULL: return "AV_ERR_NULL: a required pointer is NULL";
+    case AV_ERR_SHAPE: return "AV_ERR_SHAPE: inconsistent sizes";
+    case AV_ERR_UNSUPPORTED: return "AV_ERR_UNSUPPORTED: head dim or enum value not implemented";
+    case AV_ERR_ALIGN: return "AV_ERR_ALIGN: pointer misaligned";
+    case AV_ERR_WORKSPACE: return "AV_ERR_WORKSPACE: workspace missing or too small";
+    case AV_ERR_HIP: return "AV_ERR_HIP: the HIP runtime refused the launch";
+    case AV_ERR_PARAM: return "AV_ERR_PARAM: scalar parameter out of range";
+    case AV_ERR_TOO_LARGE: return "AV_ERR_TOO_LARGE: size exceeds 32-bit kernel addressing";
+  }
+  return "unknown av_status";
+}
+
+int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse, int B,
+             int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
+  if (var == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
+  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
+  if (var->mask < AV_MASK_NONE || var->mask > AV_MASK_DOCUMENT) return AV_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return AV_ERR_SHAPE;
+  if (var->kv_group != 0 && var->kv_group != Hq / Hkv) return AV_ERR_SHAPE;
+  if (var->mask != AV_MASK_NONE && Sq != Skv) return AV_ERR_SHAPE;
+  if (D != 32 && D != 64 && D != 128) return AV_ERR_UNSUPPORTED;
+  if (var->mask == AV_MASK_DOCUMENT && var->doc_id == nullptr) return AV_ERR_NULL;
+  if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
+  if (var->mask == AV_MASK_SLIDING_WINDOW && var->window < 1) return AV_ERR_PARAM;
+  if (var->mask == AV_MASK_PREFIX_LM && (var->prefix_len < 0 || var->prefix_len > Sq)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
+  if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
+  if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
+  // Per-slice byte offsets are 32-bit inside the kernel; query rows of a
+  // ragged last tile may index up to BM-1 rows past Sq.
+  if ((uint64_t)(Sq + av::kAttnBM) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  const int64_t nM = ((int64_t)Sq + av::kAttnBM - 1) / av::kAttnBM;
+  const int64_t total = (int64_t)B * Hq * nM;
+  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
+  if (total == 0) return AV_OK;
+
+  av::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.doc = var->doc_id;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.g = Hq / Hkv;
+  a.nM = (int)nM;
+  a.total = (int)total;
+  const double scale = var->scale > 0.f ? (double)var->scale : 1.0 / sqrt((double)D);
+  a.scale = (float)scale;
+  a.c = (float)(scale * kLog2e);
+  a.alibi_max_bias = var->alibi_max_bias;
+  a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
+  a.window = var->window;
+  a.prefix = var->prefix_len;
+  return hip_status(av::launch_attn_fwd(a, D, var->score_mod, var->mask, stream));
+}
+
+int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,
+                  float lambda, float scale, int causal, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
+  if (B <= 0 || H <= 0 || S < 0 || Dh <= 0 || Dv <= 0) return AV_ERR_SHAPE;
+  if (Dh != 64 || (Dv != 64 && Dv != 128)) return AV_ERR_UNSUPPORTED;
+  if (!isfinite(lambda)) return AV_ERR_PARAM;
+  if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
+  if ((uint64_t)(S + av::kAttnBM) * 2 * Dh * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  if ((uint64_t)(S + av::kAttnBM) * Dv * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  const int64_t nM = ((int64_t)S + av::kAttnBM - 1) / av::kAttnBM;
+  const int64_t total = (int64_t)B * H * nM;
+  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
+  if (total == 0) return AV_OK;
+  av::DiffArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.nM = (int)nM;
+  a.total = (int)total;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
+  a.c = (float)(sc * kLog2e);
+  a.lambda = lambda;
+  a.causal = causal != 0;
+  return hip_status(av::launch_diff_attn_fwd(a, Dv, stream));
+}
+
+size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh) {
+  if (Ns <= 0 || Nr <= 0 || H <= 0 || dh <= 0) return 0;
+  return av::evo_workspace_bytes(Ns, Nr, H, dh);
+}
+
+int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
+                             const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr,
+                             int Cm, int H, int dh, float scale, hipStream_t stream) {
+  if (m == nullptr || wq == nullptr || wk == nullptr || wv == nullptr || wg == nullptr || bias == nullptr ||
+      out == nullptr)
+    return AV_ERR_NULL;
+  if (Ns <= 0 || Nr <= 0 || Cm <= 0 || H <= 0 || dh <= 0) return AV_ERR_SHAPE;
+  if (dh != 32 || Cm % 64 != 0 || (H * dh) % 64 != 0) return AV_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
+  if (!aligned(m, 16) || !aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(wg, 16) ||
+      !aligned(bias, 16) || !aligned(out, 16))
+    return AV_ERR_ALIGN;
+  if ((uint64_t)Ns * Nr * Cm * 2 > kMaxSliceBytes || (uint64_t)Ns * Nr * H * dh * 2 > kMaxSliceBytes ||
+      (uint64_t)H * Nr * Nr * 2 > kMaxSliceBytes)
+    return AV_ERR_TOO_LARGE;
+  const size_t need = av::evo_workspace_bytes(Ns, Nr, H, dh);
+  if (workspace == nullptr || workspace_bytes < need) return AV_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AV_ERR_ALIGN;
+  av::EvoArgs a{};
+  a.m = m;
+  a.w[0] = wq;
+  a.w[1] = wk;
+  a.w[2] = wv;
+  a.w[3] = wg;
+  a.bias = bias;
+  a.out = out;
+  a.ws = workspace;
+  a.Ns = Ns;
+  a.Nr = Nr;
+  a.Cm = Cm;
+  a.H = H;
+  a.dh = dh;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)dh);
+  a.c = (float)(sc * kLog2e);
+  return hip_status(av::launch_evoformer(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Device-side building blocks for the gfx950 attention kernels: vector
+// types, the bf16 MFMA, raw buffer loads with hardware bounds checking,
+// exp2, cross-half wave reductions and the XCD-aware block remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace av {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs.
+constexpr uint32_t kBufferWord3 = 0x00020000u;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// Buffer resource over [base, base + bytes).  Loads at offsets >= bytes
+// return zero, which is how ragged tails are read without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+__device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Output layout used by the
+// kernels: lane l holds column n = l % 32 and rows
+//   m = 8 * (j / 4) + 4 * (l / 32) + (j % 4),  j = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// max / sum of a value with the value held by lane l ^ 32 (one
+// v_permlane32_swap plus one ALU op), result in every lane.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by block id.  Remap so
+// that XCD x processes one contiguous range of logical tiles: neighbouring
+// logical tiles (the same batch and head, hence the same K/V) then share
+// that XCD's L2.  Bijective on [0, total).
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = pid & 7, i = pid >> 3;
+  return x * q + (x < r ? x : r) + i;
+}
+
+// First index in [0, n) whose value exceeds `target` in a non-decreasing
+// int row (n when none).  All 64 lanes of the wave cooperate: each round
+// probes 64 evenly spaced positions and keeps the gap where the predicate
+// flips, so a 16k row needs three dependent loads.
+__device__ __forceinline__ int wave_upper_bound(const int* row, int n, int target) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const long long len = hi - lo;
+    const int pos = lo + (int)((len * lane) >> 6);
+    const bool le = row[pos] <= target;
+    const unsigned long long bal = __ballot(le);
+    const int c = __popcll(bal);
+    if (c == 0) {
+      hi = lo;
+      break;
+    }
+    const int p_prev = lo + (int)((len * (c - 1)) >> 6);
+    const int p_next = c < 64 ? lo + (int)((len * c) >> 6) : hi;
+    lo = p_prev + 1;
+    hi = p_next;
+  }
+  return hi;
+}
+
+__device__ __forceinline__ int wave_lower_bound(const int* row, int n, int target) {
+  return wave_upper_bound(row, n, target - 1);
+}
+
+}  // namespace av

@@ -1,0 +1,63 @@
+// Launch-side declarations shared by the C ABI (attnvar_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace av {
+
+enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2 };
+enum MaskKind : int { MK_NONE = 0, MK_CAUSAL = 1, MK_WINDOW = 2, MK_PREFIX = 3, MK_DOC = 4 };
+
+// Kernel argument block of the fused attention forward (passed by value).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;        // nullable
+  const int* doc;    // MK_DOC only
+  int B, Hq, Hkv, Sq, Skv;
+  int g;             // Hq / Hkv
+  int nM;            // query tiles per (b, head)
+  int total;         // B * Hq * nM
+  float c;           // scale * log2(e): scores are carried in log2 units
+  float scale;
+  float alibi_max_bias;
+  float softcap;
+  int window;
+  int prefix;
+};
+
+// Query rows per workgroup of the attention forward kernel.
+constexpr int kAttnBM = 128;
+
+hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
+
+struct DiffArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, H, S;
+  int nM, total;
+  float c;        // scale * log2(e)
+  float lambda;
+  int causal;
+};
+hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dv, hipStream_t stream);
+
+struct EvoArgs {
+  const void* m;
+  const void* w[4];  // wq, wk, wv, wg  [Cm, H*dh]
+  const void* bias;  // [H, Nr, Nr]
+  void* out;         // [Ns, Nr, H*dh]
+  void* ws;          // 4 x [Ns, H, Nr, dh] bf16
+  int Ns, Nr, Cm, H, dh;
+  float c;           // scale * log2(e)
+};
+size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh);
+hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream);
+
+}  // namespace av

@@ -1,0 +1,143 @@
+/*
+ * attnvar.h -- C ABI of the MI355X (gfx950) fused attention-variant library.
+ *
+ * The operations are the fused attention forward passes that the Flashlight
+ * pages describe ("Flashlight: PyTorch Compiler Extensions to Accelerate
+ * Attention Variants", MLSys 2026 talk notes, sections "Compiler design"
+ * 1-4 and "Evaluation"; Spanish summary "Resumen Tecnico: FLASHLIGHT",
+ * section "Metodologia"): QK^T, a per-element score modifier, a mask, a
+ * softmax computed online with a running max and running sum, and PV, in
+ * one kernel without writing the score matrix to memory.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer.  Memory is allocated and
+ *     owned by the caller; the library allocates nothing and frees nothing.
+ *   - Element type is bfloat16 (bf16) for every tensor unless stated;
+ *     products accumulate in fp32 (talk notes, "Implementation details",
+ *     precision item: fp16/bf16 inputs compute in fp32).
+ *   - Tensors are dense, contiguous, row-major, in the shapes given.
+ *     Tensor pointers must be 16-byte aligned; float and int32 pointers
+ *     4-byte aligned.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  The library
+ *     never synchronises.  Device faults surface at the caller's next sync.
+ *   - Every argument is validated on the host before anything is launched.
+ *     On error nothing is launched and nothing is written.
+ *   - Return value: AV_OK (0) or a negative av_status.  No C++ exception
+ *     crosses this boundary.  av_status_string() names a status.
+ *   - Calls on different streams may run concurrently; they share no state.
+ */
+#ifndef ATTNVAR_H
+#define ATTNVAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AV_OK = 0,
+  AV_ERR_NULL = -1,        /* a required pointer is NULL */
+  AV_ERR_SHAPE = -2,       /* sizes inconsistent (Hq % Hkv, Sq != Skv with a mask, negative sizes, ...) */
+  AV_ERR_UNSUPPORTED = -3, /* head dim or enum value this library does not implement */
+  AV_ERR_ALIGN = -4,       /* pointer misaligned */
+  AV_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  AV_ERR_HIP = -6,         /* the HIP runtime refused the launch */
+  AV_ERR_PARAM = -7,       /* a scalar parameter is out of range (window < 1, softcap <= 0, ...) */
+  AV_ERR_TOO_LARGE = -8    /* a size exceeds the 32-bit addressing the kernels use */
+} av_status;
+
+/* Per-element score modifiers (talk notes, "Evaluation: FlexAttention-
+ * supported variants").  Applied to the scaled score s = scale * q.k:
+ *   AV_SCORE_ALIBI:   s + slope_h * (j - i),  slope_h = 2^(-alibi_max_bias * (h+1) / Hq)
+ *                     for 0-based query head h, query row i, key row j.
+ *   AV_SCORE_SOFTCAP: softcap * tanh(s / softcap). */
+typedef enum { AV_SCORE_NONE = 0, AV_SCORE_ALIBI = 1, AV_SCORE_SOFTCAP = 2 } av_score_mod;
+
+/* Masks (same section).  Key j is visible to query i when:
+ *   AV_MASK_NONE:           always
+ *   AV_MASK_CAUSAL:         j <= i
+ *   AV_MASK_SLIDING_WINDOW: 0 <= i - j < window      (window keys, self included)
+ *   AV_MASK_PREFIX_LM:      j < prefix_len  or  j <= i
+ *   AV_MASK_DOCUMENT:       doc_id[b, i] == doc_id[b, j]   (not causal)
+ * A query row with no visible key yields an all-zero output row and
+ * lse = -inf.  Every mask other than AV_MASK_NONE needs Sq == Skv. */
+typedef enum {
+  AV_MASK_NONE = 0,
+  AV_MASK_CAUSAL = 1,
+  AV_MASK_SLIDING_WINDOW = 2,
+  AV_MASK_PREFIX_LM = 3,
+  AV_MASK_DOCUMENT = 4
+} av_mask;
+
+/* Variant descriptor: {score_mod, mask, params, kv_group}. */
+typedef struct {
+  int32_t score_mod;      /* av_score_mod */
+  int32_t mask;           /* av_mask */
+  float scale;            /* multiplies q.k; 0 selects 1/sqrt(D); must be finite and >= 0 */
+  float softcap;          /* AV_SCORE_SOFTCAP: cap > 0 */
+  float alibi_max_bias;   /* AV_SCORE_ALIBI: 8 gives slopes 2^(-8(h+1)/Hq); finite */
+  int32_t window;         /* AV_MASK_SLIDING_WINDOW: >= 1 */
+  int32_t prefix_len;     /* AV_MASK_PREFIX_LM: 0 <= prefix_len <= S */
+  const int32_t* doc_id;  /* AV_MASK_DOCUMENT: device [B, S] int32, values in [0, INT32_MAX),
+                             non-decreasing along each row (a precondition the host cannot
+                             check: rows that break it give unspecified output) */
+  int32_t kv_group;       /* Hq / Hkv (1 = MHA); 0 = derive from Hq and Hkv */
+} av_variant;
+
+/* Fused attention forward, MHA and GQA.
+ *   q   [B, Hq,  Sq,  D]    k [B, Hkv, Skv, D]    v [B, Hkv, Skv, D]
+ *   out [B, Hq,  Sq,  D]    written (bf16, round-to-nearest-even from fp32)
+ *   lse [B, Hq,  Sq]  fp32  natural-log sum-exp of the modified, masked
+ *                           scores per row; may be NULL (not written).
+ * Query head h reads key/value head h / (Hq / Hkv).  D in {32, 64, 128}.
+ * Sq == 0 launches nothing; Skv == 0 writes zero rows and lse = -inf.
+ * Each (b, Hkv head) slice of K and V, and each (b, Hq head) slice of Q
+ * and out, must be smaller than 2 GiB. */
+int attn_fwd(const av_variant* variant, const void* q, const void* k, const void* v, void* out,
+             float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream);
+
+/* Differential attention forward (talk notes, "Background and motivation"
+ * and "Evaluation: complex attention variants"; the pages name the variant
+ * without a formula; the reading implemented is):
+ *   q, k [B, H, S, 2*Dh]: two halves q1 = q[..., :Dh], q2 = q[..., Dh:]
+ *   v    [B, H, S, Dv],  out [B, H, S, Dv]
+ *   out = (softmax(scale * q1 k1^T + M) - lambda * softmax(scale * q2 k2^T + M)) v
+ * M is the causal mask when `causal` != 0, else nothing.  scale = 0 selects
+ * 1/sqrt(Dh).  Supported: Dh = 64, Dv in {64, 128}. */
+int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh,
+                  int Dv, float lambda, float scale, int causal, hipStream_t stream);
+
+/* Evoformer row-wise gated self-attention with pair bias (talk notes,
+ * "Evaluation: complex attention variants" and the AlphaFold2 end-to-end
+ * section; no formula on the pages; the reading implemented is, per MSA
+ * sequence s, head h, residue rows i, j):
+ *   q, k, v, g = m Wq, m Wk, m Wv, m Wg                 (no bias, no LayerNorm)
+ *   out[s, i, h*dh + e] = sigmoid(g[s, i, h*dh + e])
+ *                         * sum_j softmax_j(scale * q_i.k_j + bias[h, i, j]) v_j[e]
+ *   m    [Ns, Nr, Cm]      w* [Cm, H*dh] each      bias [H, Nr, Nr]
+ *   out  [Ns, Nr, H*dh]
+ * The projections are computed into `workspace` (bf16, owned by the caller,
+ * at least evoformer_workspace_bytes(...) bytes, 256-byte aligned) by one
+ * kernel, then consumed by the attention kernel.  scale = 0 selects
+ * 1/sqrt(dh).  Supported: dh = 32, Cm a multiple of 64, H*dh a multiple of 64. */
+size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh);
+int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
+                             const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns,
+                             int Nr, int Cm, int H, int dh, float scale, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* av_status_string(int status);
+
+/* ABI version of this header; bumped when a signature or struct changes. */
+#define AV_ABI_VERSION 1
+int av_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNVAR_H */

@@ -1,0 +1,149 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function ``include/attnvar.h`` declares, and rejects every invalid argument
+with the documented status before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_variants_amd as av
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "attnvar.h")
+
+# Fake, aligned, non-null device addresses: validation fails before any use.
+P = 0x10000
+P2 = 0x20000
+P3 = 0x30000
+P4 = 0x40000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return av.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(av.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.av_abi_version() == 1
+    for code, name in av.STATUS.items():
+        assert lib.av_status_string(code).decode().startswith(name)
+    assert lib.av_status_string(12345).decode() == "unknown av_status"
+
+
+def _attn(lib, var=None, q=P, k=P2, v=P3, o=P4, lse=None, B=1, Hq=2, Hkv=2, Sq=128, Skv=128, D=64):
+    if var is None:
+        var = av.make_variant()
+    ref = None if var == "null" else ctypes.byref(var)
+    return lib.attn_fwd(ref, q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, None)
+
+
+def test_attn_fwd_rejections(lib):
+    assert _attn(lib, var="null") == -1
+    assert _attn(lib, q=None) == -1
+    assert _attn(lib, k=None) == -1
+    assert _attn(lib, v=None) == -1
+    assert _attn(lib, o=None) == -1
+    assert _attn(lib, av.make_variant(mask="document")) == -1  # doc_id missing
+    # shapes
+    assert _attn(lib, B=0) == -2
+    assert _attn(lib, Hq=3, Hkv=2) == -2
+    assert _attn(lib, Sq=-1) == -2
+    assert _attn(lib, av.make_variant(kv_group=3), Hq=4, Hkv=2) == -2
+    assert _attn(lib, av.make_variant(kv_group=2), Hq=4, Hkv=2, Sq=0) == 0  # empty: nothing launched
+    assert _attn(lib, av.make_variant(mask="causal"), Sq=128, Skv=64) == -2
+    # unsupported
+    assert _attn(lib, D=48) == -3
+    assert _attn(lib, D=256) == -3
+    bad = av.make_variant()
+    bad.score_mod = 7
+    assert _attn(lib, bad) == -3
+    bad = av.make_variant()
+    bad.mask = -1
+    assert _attn(lib, bad) == -3
+    # params
+    assert _attn(lib, av.make_variant(score_mod="softcap", softcap=0.0)) == -7
+    assert _attn(lib, av.make_variant(score_mod="softcap", softcap=float("nan"))) == -7
+    assert _attn(lib, av.make_variant(scale=-1.0)) == -7
+    assert _attn(lib, av.make_variant(scale=float("inf"))) == -7
+    assert _attn(lib, av.make_variant(score_mod="alibi", alibi_max_bias=float("inf"))) == -7
+    assert _attn(lib, av.make_variant(mask="sliding_window", window=0)) == -7
+    assert _attn(lib, av.make_variant(mask="prefix_lm", prefix_len=129)) == -7
+    assert _attn(lib, av.make_variant(mask="prefix_lm", prefix_len=-1)) == -7
+    # alignment
+    assert _attn(lib, q=P + 8) == -4
+    assert _attn(lib, o=P4 + 2) == -4
+    assert _attn(lib, lse=P + 2) == -4
+    # sizes beyond 32-bit slice addressing
+    assert _attn(lib, Sq=1 << 24, Skv=1 << 24, D=128) == -8
+    assert _attn(lib, Skv=1 << 24, D=128) == -8
+    # empty query set is a no-op success
+    assert _attn(lib, Sq=0, Skv=0) == 0
+
+
+def test_diff_attn_rejections(lib):
+    def call(q=P, k=P2, v=P3, o=P4, B=1, H=2, S=64, Dh=64, Dv=128, lam=0.8, scale=0.0):
+        return lib.diff_attn_fwd(q, k, v, o, B, H, S, Dh, Dv, lam, scale, 1, None)
+
+    assert call(q=None) == -1
+    assert call(o=None) == -1
+    assert call(B=0) == -2
+    assert call(S=-3) == -2
+    assert call(Dh=32) == -3
+    assert call(Dv=96) == -3
+    assert call(lam=float("nan")) == -7
+    assert call(scale=-2.0) == -7
+    assert call(k=P2 + 4) == -4
+    assert call(S=0) == 0
+
+
+def test_evoformer_rejections(lib):
+    need = lib.evoformer_workspace_bytes(128, 256, 8, 32)
+    assert need == 4 * 128 * 256 * 8 * 32 * 2
+    assert lib.evoformer_workspace_bytes(0, 256, 8, 32) == 0
+
+    def call(m=P, w=P2, bias=P3, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=2, dh=32, scale=0.0):
+        if wsb is None:
+            wsb = lib.evoformer_workspace_bytes(max(Ns, 1), max(Nr, 1), max(H, 1), max(dh, 1))
+        return lib.evoformer_gated_attn_fwd(m, w, w, w, w, bias, out, ws, wsb, Ns, Nr, Cm, H, dh, scale, None)
+
+    assert call(m=None) == -1
+    assert call(w=None) == -1
+    assert call(bias=None) == -1
+    assert call(Ns=0) == -2
+    assert call(dh=64) == -3
+    assert call(Cm=48) == -3
+    assert call(scale=float("nan")) == -7
+    assert call(m=P + 2) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=100) == -5
+    assert call(ws=0x100000 + 16) == -4
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        av.attn_fwd(x, x, x)
+    with pytest.raises(ValueError):
+        av.make_variant(mask="bogus")
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError):
+        av.load_library(str(tmp_path / "nope.so"))
