@@ -42,7 +42,10 @@ const char* av_status_string(int status) {
 
 int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse, int B,
              int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
-  if (var == nullptr || q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
+  if (var == nullptr) return AV_ERR_NULL;
+  // Empty tensors may come with NULL data pointers: only sizes > 0 need memory.
+  if ((Sq > 0 && (q == nullptr || out == nullptr)) || (Skv > 0 && (k == nullptr || v == nullptr)))
+    return AV_ERR_NULL;
   if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
   if (var->mask < AV_MASK_NONE || var->mask > AV_MASK_DOCUMENT) return AV_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;

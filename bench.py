@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = the hot path over the headline workload: the MHA score-modifier
+shape at S = 4096 (B = 4, H = 16, D = 64, 16k tokens), run once per score
+modifier (vanilla, ALiBi, tanh softcap).  Inputs are seeded synthetic bf16
+N(0,1) tensors resident in HBM before timing starts.  Prints ONE JSON line.
+
+Throughput is visible (unmasked) FLOPs / time: 4 * D flops per visible
+(query, key) pair (QK^T and PV).  The roofline block covers the slowest of
+the three kernels, timed with HIP events on the launch stream; the CPU
+baseline is the fp64 oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --sweep OUT.jsonl     (all shapes of every variant, one line each)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from workloads import inputs as wi  # noqa: E402
+
+METRIC = "attention fwd TFLOP/s (visible FLOPs) & % bf16 MFMA peak, per variant"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("attention_variants_amd/csrc/attn_fwd.hip", "attention_variants_amd/csrc/av_device.hpp")
+
+
+# ----------------------------------------------------------------- work model
+def visible_pairs(mask, S, *, window=256, prefix_len=0, doc_lens=None):
+    """Number of visible (query, key) pairs of one head."""
+    if mask == "none":
+        return S * S
+    if mask == "causal":
+        return S * (S + 1) // 2
+    if mask == "sliding_window":
+        W = min(window, S)
+        return W * (W + 1) // 2 + (S - W) * W
+    if mask == "prefix_lm":
+        P = prefix_len
+        return P * P + (S * (S + 1) // 2 - P * (P + 1) // 2)
+    if mask == "document":
+        return sum(L * L for L in doc_lens)
+    raise ValueError(mask)
+
+
+def attn_flops(B, Hq, S, D, mask, **kw):
+    if mask == "document":
+        return sum(visible_pairs(mask, S, doc_lens=lens) for lens in kw["doc_lens"]) * Hq * 4 * D
+    return B * Hq * visible_pairs(mask, S, **kw) * 4 * D
+
+
+def attn_bytes(B, Hq, Hkv, S, D):
+    return 2 * (2 * B * Hq * S * D + 2 * B * Hkv * S * D)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_vanilla_S4096_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- GPU timing
+def _dev(bits, dev):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_launches(fns, steps, warmup):
+    """Run each callable of `fns` once per step; return (total_ms, [per-fn mean ms])."""
+    import torch
+
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    starts = [[torch.cuda.Event(enable_timing=True) for _ in range(steps)] for _ in fns]
+    ends = [[torch.cuda.Event(enable_timing=True) for _ in range(steps)] for _ in fns]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for s in range(steps):
+        for i, f in enumerate(fns):
+            starts[i][s].record()
+            f()
+            ends[i][s].record()
+    t1.record()
+    torch.cuda.synchronize()
+    total = t0.elapsed_time(t1)
+    per = [sum(starts[i][s].elapsed_time(ends[i][s]) for s in range(steps)) / steps for i in range(len(fns))]
+    return total, per
+
+
+# ----------------------------------------------------------------- CPU baseline
+def cpu_baseline(budget_s=15.0):
+    """The fp64 oracle, unchanged, on a bounded sample of the workload: whole
+    heads of the S=4096 shape, cycling vanilla/ALiBi/softcap, until the time
+    budget is spent.  Rate = visible FLOPs of the heads done / wall time."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        threads = 1
+    S, D = 4096, 64
+    x = wi.attention_inputs(1, 2, 2, S, S, D)
+    q, k, v = (wi.bf16_bits_to_f64(x[n]) for n in ("q", "k", "v"))
+    mods = ("none", "alibi", "softcap")
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        sm = mods[done % 3]
+        h = (done // 3) % 2
+        oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], score_mod=sm)
+        done += 1
+        flops += S * S * 4 * D
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} whole heads (S=4096, D=64, all 4096 query rows) cycling vanilla/ALiBi/softcap, "
+                  f"{dt:.1f} s wall, fp64 numpy; host os.cpu_count()={os.cpu_count()}",
+    }
+
+
+# ----------------------------------------------------------------- main bench
+def run_headline(args):
+    import torch
+
+    import attention_variants_amd as av
+
+    av.load_library()
+    dev = torch.device("cuda:0")
+    B, H, S, D = 4, 16, 4096, 64
+    x = wi.attention_inputs(B, H, H, S, S, D)
+    q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    mods = ("none", "alibi", "softcap")
+    fns = [(lambda sm=sm: av.attn_fwd(q, k, v, score_mod=sm, out=out)) for sm in mods]
+    total_ms, per_ms = time_launches(fns, args.steps, args.warmup)
+    fl = attn_flops(B, H, S, D, "none")
+    ms_step = total_ms / args.steps
+    value = 3 * fl / (ms_step * 1e-3) / 1e12
+    variants = {}
+    for sm, ms in zip(mods, per_ms):
+        tf = fl / (ms * 1e-3) / 1e12
+        variants[sm] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    dom = max(range(3), key=lambda i: per_ms[i])
+    achieved = fl / (per_ms[dom] * 1e-3) / 1e12
+    traffic = measured_traffic() if mods[dom] == "none" else None
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "mha_score_mod_S4096",
+            "B": B, "H": H, "S": S, "D": D,
+            "variants": list(mods),
+            "step": "one attn_fwd per score modifier (vanilla, ALiBi, softcap), no mask",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"attn_fwd_kernel<D=64, score_mod={mods[dom]}, mask=none>",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(per_ms[dom] * 1e3, 2),
+            "algorithmic_flops_per_launch": fl,
+            "algorithmic_bytes_per_launch": attn_bytes(B, H, H, S, D),
+        },
+        "variants": variants,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def run_sweep(path, steps, warmup):
+    """Every shape of every variant (score mods, masks MHA/GQA, diff, Evoformer); one JSON line each."""
+    import torch
+
+    import attention_variants_amd as av
+
+    av.load_library()
+    dev = torch.device("cuda:0")
+    f = open(path, "w")
+
+    def emit(rec):
+        f.write(json.dumps(rec) + "\n")
+        f.flush()
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+
+    for S in (512, 1024, 2048, 4096, 8192, 16384):
+        B = 16384 // S
+        for Hkv in (16, 2):
+            x = wi.attention_inputs(B, 16, Hkv, S, S, 64)
+            q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+            out = torch.empty_like(q)
+            doc_np = wi.doc_ids(4, B, S)
+            doc = torch.from_numpy(doc_np).to(dev)
+            doc_lens = wi.doc_lengths(4, B, S)
+            cases = [("none", "none"), ("alibi", "none"), ("softcap", "none")] if Hkv == 16 else []
+            cases += [("none", "causal"), ("none", "sliding_window"), ("none", "prefix_lm"), ("none", "document")]
+            for sm, mk in cases:
+                kw = dict(score_mod=sm, mask=mk, window=256, prefix_len=S // 4,
+                          doc_id=doc if mk == "document" else None, out=out)
+                _, per = time_launches([lambda kw=kw: av.attn_fwd(q, k, v, **kw)], steps, warmup)
+                fl = attn_flops(B, 16, S, 64, mk, window=256, prefix_len=S // 4, doc_lens=doc_lens)
+                by = attn_bytes(B, 16, Hkv, S, 64)
+                tf = fl / (per[0] * 1e-3) / 1e12
+                emit({"kernel": "attn_fwd", "score_mod": sm, "mask": mk, "B": B, "Hq": 16, "Hkv": Hkv, "S": S,
+                      "D": 64, "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
+                      "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                      "hbm_gbs": round(by / (per[0] * 1e-3) / 1e9, 1)})
+    for S in (1024, 4096, 16384):
+        B = 16384 // S
+        x = wi.diff_inputs(B, 16, S)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(v)
+        try:
+            _, per = time_launches([lambda: av.diff_attn_fwd(q, k, v, out=out)], steps, warmup)
+        except RuntimeError as e:  # not built in this library version
+            emit({"kernel": "diff_attn_fwd", "S": S, "error": str(e)})
+            continue
+        pairs = B * 16 * S * (S + 1) // 2
+        tf = pairs * 512 / (per[0] * 1e-3) / 1e12
+        emit({"kernel": "diff_attn_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
+              "visible_tflops": round(tf, 1), "executed_tflops": round(tf * 1.5, 1),
+              "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+    for Nr in (256, 384, 768):
+        Ns, Cm, Hh, dh = 128, 256, 8, 32
+        x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
+        t = {n: _dev(x[n], dev) for n in x}
+        ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
+        out = torch.empty((Ns, Nr, Hh * dh), dtype=torch.bfloat16, device=dev)
+        try:
+            _, per = time_launches([lambda: av.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"],
+                                                                        t["bias"], H=Hh, dh=dh, workspace=ws,
+                                                                        out=out)], steps, warmup)
+        except RuntimeError as e:
+            emit({"kernel": "evoformer", "Nr": Nr, "error": str(e)})
+            continue
+        fl = 2 * Ns * Nr * Cm * 4 * Hh * dh + 4 * Ns * Hh * Nr * Nr * dh
+        tf = fl / (per[0] * 1e-3) / 1e12
+        emit({"kernel": "evoformer_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "us": round(per[0] * 1e3, 2),
+              "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+    f.close()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 (no multi-GPU path exists)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        run_sweep(args.sweep, args.steps, args.warmup)
+        return
+    rec = run_headline(args)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

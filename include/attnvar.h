@@ -95,6 +95,7 @@ typedef struct {
  *                           scores per row; may be NULL (not written).
  * Query head h reads key/value head h / (Hq / Hkv).  D in {32, 64, 128}.
  * Sq == 0 launches nothing; Skv == 0 writes zero rows and lse = -inf.
+ * Pointers of empty tensors may be NULL (q/out when Sq == 0, k/v when Skv == 0).
  * Each (b, Hkv head) slice of K and V, and each (b, Hq head) slice of Q
  * and out, must be smaller than 2 GiB. */
 int attn_fwd(const av_variant* variant, const void* q, const void* k, const void* v, void* out,

@@ -58,6 +58,7 @@ def test_attn_fwd_rejections(lib):
     assert _attn(lib, k=None) == -1
     assert _attn(lib, v=None) == -1
     assert _attn(lib, o=None) == -1
+    assert _attn(lib, k=None, v=None, Skv=0, Sq=0) == 0  # empty tensors may be NULL
     assert _attn(lib, av.make_variant(mask="document")) == -1  # doc_id missing
     # shapes
     assert _attn(lib, B=0) == -2
