@@ -15,20 +15,23 @@
 //    each wave owns 32 rows for the whole KV loop.
 //  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //    MFMA.  In its output layout every lane holds 16 keys of ONE query
-//    (lanes l and l^32 share the query), so the row max and row sum are
-//    in-register reductions plus one v_permlane32_swap, and the exponentiated
-//    tile feeds the second MFMA (O^T = V^T P^T) straight from registers as
-//    its B operand: no LDS round trip for P.
-//  * K tiles sit in LDS row-major; V tiles are stored transposed (V^T) so
-//    the A operand of O^T += V^T P^T is one 16-byte LDS read per lane.
-//    Keys inside each 16-key group are permuted (bits 2 and 3 swapped) to
-//    match the order in which the S^T output layout holds them.  Both tiles
-//    use an XOR swizzle of their 16-byte groups against bank conflicts and
-//    are double-buffered, with the next tile's global loads in flight while
-//    the current one is computed.
-//  * Scores are carried in log2 units (scale * log2 e folded in), exp2 is
-//    the hardware v_exp_f32, accumulation is fp32 (talk notes,
-//    "Implementation details", precision item).
+//    (lanes l and l^32 share the query), so the row max is an in-register
+//    reduction plus one v_permlane32_swap, and the exponentiated tile feeds
+//    the second MFMA (O^T = V^T P^T) straight from registers as its B
+//    operand: no LDS round trip for P.
+//  * K and V tiles sit row-major in LDS (padded pitches, conflict-free for
+//    the read patterns below), double-buffered, with the next tile's global
+//    loads in flight while the current one is computed.  The V^T operand is
+//    read with gfx950's transposed LDS read, two per MFMA.
+//  * Scores are carried in log2 units (scale * log2 e folded in); exp2 is the
+//    hardware v_exp_f32; accumulation is fp32 (talk notes, "Implementation
+//    details", precision item).
+//  * The running max used as the exponent reference is only raised when a
+//    tile's max exceeds it by more than 2^8 (then O and l are rescaled);
+//    otherwise the exponentials stay below 256 and no rescale is paid.  The
+//    result is the same softmax: every exponential and the sum share one
+//    reference.  The row sum adds the bf16-rounded probabilities, exactly the
+//    values the PV product consumes.
 //  * Masks are analytic: each workgroup computes the KV tile range that
 //    holds any visible key (document masks: two 64-way wave searches over
 //    the doc-id row), each wave classifies every tile as skipped, full (no
@@ -40,6 +43,8 @@
 //    made XCD-aware); causal and PrefixLM grids start with the heaviest query
 //    tiles.
 
+#include <type_traits>
+
 #include "av_device.hpp"
 #include "av_kernels.hpp"
 
@@ -49,30 +54,27 @@ namespace {
 constexpr int BM = kAttnBM;  // query rows per workgroup
 constexpr int BN = 64;       // keys per KV tile
 constexpr int NT = 256;      // threads per workgroup
+constexpr float kTau = 8.f;  // lazy-rescale threshold, log2 units
 
-// Position of key r (0..BN-1) inside the V^T tile: bits 2 and 3 swapped.
-__device__ __forceinline__ int vt_pos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Physical 16-byte group of logical group `gi` in row `row`.
 template <int D>
-__device__ __forceinline__ int k_swz(int row, int gi) {
-  constexpr int kMask = (D / 8 >= 8) ? 7 : (D / 8 - 1);
-  return gi ^ (row & kMask);
+constexpr int min_waves() {
+  return D <= 64 ? 2 : 1;
 }
-__device__ __forceinline__ int vt_swz(int d, int gi) { return gi ^ ((d ^ (d >> 3)) & 7); }
 
 template <int D, int SM, int MK>
-__global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
   constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int NDS = D / 16;        // k-steps of the QK^T MFMA
   constexpr int NPS = BN / 16;       // k-steps of the PV MFMA
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   constexpr int NCH = BN * CPR / NT; // chunks per thread per tensor
+  constexpr int KP = D + 8;          // K row pitch (elements): 8 rows hit 8 distinct 16-byte bank groups
+  constexpr int VP = D + 16;         // V row pitch: 4 rows hit 4 distinct 32-byte bank groups
   static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile/thread mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * BN];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * VP];
   __shared__ __attribute__((aligned(16))) int Ds[2][MK == MK_DOC ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
   const int hk = hq / a.g;
   const int mt = (MK == MK_CAUSAL || MK == MK_PREFIX) ? (a.nM - 1 - mt_lin) : mt_lin;
   const int q0 = mt * BM;
-  const int qw = q0 + 32 * w;          // first query row of this wave
-  const int qi = qw + l32;             // this lane's query row
+  const int qw = q0 + 32 * __builtin_amdgcn_readfirstlane(w);  // first query row of this wave
+  const int qi = qw + l32;                                       // this lane's query row
   const int qlast = min(q0 + BM, a.Sq) - 1;
   const bool wave_live = qw < a.Sq;
   const int qwlast = min(qw + 31, a.Sq - 1);
@@ -117,8 +119,8 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
     n_lo = kstart / BN;
     n_hi = min(nKV, (kend + BN - 1) / BN);
     dq = docrow[min(qi, a.Sq - 1)];
-    dqw = docrow[min(qw, a.Sq - 1)];
-    dqwlast = docrow[max(qwlast, 0)];
+    dqw = __builtin_amdgcn_readfirstlane(docrow[min(qw, a.Sq - 1)]);
+    dqwlast = __builtin_amdgcn_readfirstlane(docrow[max(qwlast, 0)]);
   }
 
   // ---- Q^T operands in registers: lane holds query qi, 8 consecutive d per k-step
@@ -132,14 +134,24 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m_run = neg_inf();  // running max (log2 units), identical in lanes l and l^32
-  float l_run = 0.f;        // running sum over this lane's keys only
+  float m_ref = neg_inf();  // exponent reference (log2 units), identical in lanes l and l^32
+  float m_sub = 0.f;        // m_ref with -inf replaced by 0 (the value subtracted in exp2)
+  float l_run = 0.f;        // sum of this lane's bf16 probabilities, relative to m_ref
 
+  // score-modifier constants
   float alibi_slope2 = 0.f;
-  if constexpr (SM == SM_ALIBI)
-    alibi_slope2 = kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq);
-  const float cap2 = a.softcap * kLog2e;
+  float alibi_k[NKB * 16];  // slope * key offset of each S^T register (wave-uniform)
+  if constexpr (SM == SM_ALIBI) {
+    alibi_slope2 = uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq));
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) alibi_k[kb * 16 + j] = uniform_f(alibi_slope2 * (float)(kb * 32 + 8 * (j >> 2) + (j & 3)));
+  }
+  const float cap2 = a.softcap * kLog2e;            // softcap in log2 units
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
+  // cap * log2e * tanh(raw * scale / cap) from exp2 and rcp
+  auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap2); };
 
   i32x4 kr[NCH], vr[NCH];
   int dr = 0;
@@ -165,17 +177,124 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
     for (int c = 0; c < NCH; ++c) {
       const int idx = tid + NT * c;
       const int row = idx / CPR, col = idx % CPR;
-      *(i32x4*)&Ks[buf][row * D + k_swz<D>(row, col) * 8] = kr[c];
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vr[c]);
-      const int p = vt_pos(row);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = col * 8 + e;
-        Vt[buf][d * BN + vt_swz(d, p >> 3) * 8 + (p & 7)] = vv[e];
-      }
+      *(i32x4*)&Ks[buf][row * KP + col * 8] = kr[c];
+      *(i32x4*)&Vs[buf][row * VP + col * 8] = vr[c];
     }
     if constexpr (MK == MK_DOC) {
       if (tid < BN) Ds[buf][tid] = dr;
+    }
+  };
+
+  // per-lane parts of the transposed V read: rows 4*hh + r/4 (+8), columns 16*g + 4*(r%4)
+  const int r16 = lane & 15;
+  const int v_row0 = 4 * hh + (r16 >> 2);
+  const int v_col0 = 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
+
+  auto tile = [&](auto full_c, int buf, int n0) {
+    constexpr bool FULL = decltype(full_c)::value;
+    // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      const bf16* krow = &Ks[buf][(kb * 32 + l32) * KP + hh * 8];
+#pragma unroll
+      for (int st = 0; st < NDS; ++st) s[kb] = mfma32(*(const bf16x8*)(krow + st * 16), qreg[st], s[kb]);
+    }
+
+    // ---- score modifier, mask, tile row max
+    const int kbase = n0 + 4 * hh;
+    const float alibi_base = (SM == SM_ALIBI) ? alibi_slope2 * (float)(kbase - qi) : 0.f;
+    float tmax = neg_inf();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+        float x = s[kb][j];
+        if constexpr (SM == SM_ALIBI) x = fmaf(x, a.c, alibi_k[kb * 16 + j]);
+        if constexpr (SM == SM_SOFTCAP && !FULL) x = softcap_t(x);
+        if constexpr (!FULL) {
+          bool ok = off < a.Skv - kbase;
+          if constexpr (MK == MK_CAUSAL) {
+            ok = ok && (off <= qi - kbase);
+          } else if constexpr (MK == MK_WINDOW) {
+            const int rel = qi - kbase;
+            ok = ok && (off <= rel) && (off > rel - a.window);
+          } else if constexpr (MK == MK_PREFIX) {
+            ok = ok && ((off < a.prefix - kbase) || (off <= qi - kbase));
+          } else if constexpr (MK == MK_DOC) {
+            ok = ok && (Ds[buf][off + 4 * hh] == dq);
+          }
+          x = ok ? x : neg_inf();
+        }
+        s[kb][j] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    }
+    float tile_max;  // log2 units
+    if constexpr (SM == SM_NONE) {
+      tile_max = xhalf_max(tmax) * a.c;
+    } else if constexpr (SM == SM_ALIBI) {
+      tile_max = xhalf_max(tmax + alibi_base);
+    } else if constexpr (FULL) {
+      tile_max = xhalf_max(softcap_t(tmax));  // tanh is monotone: cap the raw max
+    } else {
+      tile_max = xhalf_max(tmax);
+    }
+
+    // ---- lazy rescale: raise the reference only when the max grew by > 2^kTau
+    if (any_lane(tile_max > m_ref + kTau)) {
+      const float m_new = fmaxf(m_ref, tile_max);
+      const float m_new_sub = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_ref - m_new_sub);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+      m_ref = m_new;
+      m_sub = m_new_sub;
+    }
+
+    // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
+    bf16x8 pb[NPS];
+    const float mb = m_sub - alibi_base;       // ALiBi: fold the per-lane bias base into the reference
+    const float cm = cap2 - m_sub;             // softcap, full tiles
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        float p0, p1;
+        if constexpr (SM == SM_NONE) {
+          p0 = exp2_fast(fmaf(s[kb][j], a.c, -m_sub));
+          p1 = exp2_fast(fmaf(s[kb][j + 1], a.c, -m_sub));
+        } else if constexpr (SM == SM_ALIBI) {
+          p0 = exp2_fast(s[kb][j] - mb);
+          p1 = exp2_fast(s[kb][j + 1] - mb);
+        } else if constexpr (FULL) {
+          p0 = exp2_fast(fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(s[kb][j] * sc_k)), cm));
+          p1 = exp2_fast(fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(s[kb][j + 1] * sc_k)), cm));
+        } else {
+          p0 = exp2_fast(s[kb][j] - m_sub);
+          p1 = exp2_fast(s[kb][j + 1] - m_sub);
+        }
+        const bf16x2 pp = {(bf16)p0, (bf16)p1};
+        l_run = add_bf16_pair(pp, l_run);
+        pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
+        pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+      }
+    }
+
+    // ---- O^T += V^T P^T, V^T operand via two transposed LDS reads per MFMA
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int t = 0; t < NPS; ++t) {
+        const bf16* vp = &Vs[buf][((t >> 1) * 32 + 16 * (t & 1) + v_row0) * VP + db * 32 + v_col0];
+        const i16x4 lo = lds_read_tr16(vp);
+        const i16x4 hi = lds_read_tr16(vp + 8 * VP);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[db] = mfma32(vf, pb[t], o[db]);
+      }
     }
   };
 
@@ -205,94 +324,11 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
       skip |= (d1 < dqw) || (d0 > dqwlast);
       full &= (d0 == dqw) && (d1 == dqwlast) && (dqw == dqwlast);
     }
-    if (skip) continue;
-
-    // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const int row = kb * 32 + l32;
-#pragma unroll
-      for (int st = 0; st < NDS; ++st) {
-        const bf16x8 kf = *(const bf16x8*)&Ks[buf][row * D + k_swz<D>(row, st * 2 + hh) * 8];
-        s[kb] = mfma32(kf, qreg[st], s[kb]);
-      }
-    }
-
-    // ---- score modifier, mask, tile row max
-    const int kbase = n0 + 4 * hh;
-    float tmax = neg_inf();
-    float alibi_base = 0.f;
-    if constexpr (SM == SM_ALIBI) alibi_base = alibi_slope2 * (float)(kbase - qi);
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-        float x = s[kb][j];
-        if constexpr (SM == SM_ALIBI) {
-          x = fmaf(x, a.c, fmaf(alibi_slope2, (float)off, alibi_base));
-        } else if constexpr (SM == SM_SOFTCAP) {
-          const float e = exp2_fast(x * sc_k);
-          x = fmaf(-2.f * cap2, rcp_fast(1.f + e), cap2);
-        }
-        if (!full) {
-          bool ok = off < a.Skv - kbase;
-          if constexpr (MK == MK_CAUSAL) {
-            ok = ok && (off <= qi - kbase);
-          } else if constexpr (MK == MK_WINDOW) {
-            const int rel = qi - kbase;
-            ok = ok && (off <= rel) && (off > rel - a.window);
-          } else if constexpr (MK == MK_PREFIX) {
-            ok = ok && ((off < a.prefix - kbase) || (off <= qi - kbase));
-          } else if constexpr (MK == MK_DOC) {
-            ok = ok && (Ds[buf][off + 4 * hh] == dq);
-          }
-          x = ok ? x : neg_inf();
-        }
-        s[kb][j] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    }
-    tmax = xhalf_max(tmax);
-    const float tile_max = (SM == SM_NONE) ? tmax * a.c : tmax;
-    const float m_new = fmaxf(m_run, tile_max);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
-
-    // ---- p = exp2(t - m); running sum; P^T operands in bf16
-    bf16x8 pb[NPS];
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float p;
-        if constexpr (SM == SM_NONE) {
-          p = exp2_fast(fmaf(s[kb][j], a.c, -m_use));
-        } else {
-          p = exp2_fast(s[kb][j] - m_use);
-        }
-        psum += p;
-        pb[kb * 2 + (j >> 3)][j & 7] = (bf16)p;
-      }
-    }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < NPS; ++t) {
-        const bf16x8 vf = *(const bf16x8*)&Vt[buf][d * BN + vt_swz(d, t * 2 + hh) * 8];
-        o[db] = mfma32(vf, pb[t], o[db]);
-      }
-    }
+    if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+    if (__builtin_amdgcn_readfirstlane((int)full))
+      tile(std::true_type{}, buf, n0);
+    else
+      tile(std::false_type{}, buf, n0);
   }
 
   // ---- epilogue: O / l, bf16 store, optional LSE
@@ -311,7 +347,7 @@ __global__ __launch_bounds__(NT, 2) void attn_fwd_kernel(const AttnArgs a) {
       }
     }
     if (a.lse != nullptr && hh == 0) {
-      a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : neg_inf();
+      a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
     }
   }
 }

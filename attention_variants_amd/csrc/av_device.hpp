@@ -14,6 +14,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -41,6 +43,27 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transposed LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane r supplies the address of 4 consecutive 16-bit values (row r of a
+// 16 x 4 block M); lane i receives M[i/4][i%4], M[4+i/4][i%4], M[8+i/4][i%4],
+// M[12+i/4][i%4].  Pointing lane r at V[k0 + r/4][c0 + 4*(r%4)] of a
+// row-major tile therefore hands lane i the four values V[k0..k0+3][c0 + i]:
+// a column of V, which is what a B-transposed MFMA operand needs.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// Sum of two bf16 values accumulated in fp32 (v_dot2_f32_bf16 against 1, 1).
+__device__ __forceinline__ float add_bf16_pair(bf16x2 p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+}
+
+__device__ __forceinline__ float uniform_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+__device__ __forceinline__ bool any_lane(bool b) { return __builtin_amdgcn_ballot_w64(b) != 0; }
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // max / sum of a value with the value held by lane l ^ 32 (one
