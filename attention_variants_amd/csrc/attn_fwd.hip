@@ -43,8 +43,6 @@
 //    made XCD-aware); causal and PrefixLM grids start with the heaviest query
 //    tiles.
 
-#include <type_traits>
-
 #include "av_device.hpp"
 #include "av_kernels.hpp"
 
@@ -56,13 +54,18 @@ constexpr int BN = 64;       // keys per KV tile
 constexpr int NT = 256;      // threads per workgroup
 constexpr float kTau = 8.f;  // lazy-rescale threshold, log2 units
 
-template <int D>
+// Waves per SIMD each instantiation's register budget is sized for.  Four
+// (<= 128 VGPRs; the LDS of four 38 KB workgroups also fits a CU) where the
+// code fits without spilling, else three (<= 168 VGPRs); two at D = 128.
+template <int D, int SM, int MK>
 constexpr int min_waves() {
-  return D <= 64 ? 2 : 1;
+  if (D <= 32) return 4;
+  if (D == 64) return (SM == SM_NONE && (MK == MK_NONE || MK == MK_CAUSAL || MK == MK_WINDOW)) ? 4 : 3;
+  return 2;
 }
 
 template <int D, int SM, int MK>
-__global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
   constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int NDS = D / 16;        // k-steps of the QK^T MFMA
@@ -139,16 +142,17 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
   float l_run = 0.f;        // sum of this lane's bf16 probabilities, relative to m_ref
 
   // score-modifier constants
+  // ALiBi, log2 units: bias(kb, j) = slope * (kj - qi) with kj = n0 + 4*hh + 32*kb + 8*(j/4) + j%4
+  //   = [slope * (n0 + 4*hh - qi + j%4)]  (4 per-lane values per tile)
+  //   + [slope * (32*kb + 8*(j/4))]       (wave-uniform, one SGPR each)
   float alibi_slope2 = 0.f;
-  float alibi_k[NKB * 16];  // slope * key offset of each S^T register (wave-uniform)
+  float alibi_u[NKB * 4];
   if constexpr (SM == SM_ALIBI) {
     alibi_slope2 = uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq));
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) alibi_k[kb * 16 + j] = uniform_f(alibi_slope2 * (float)(kb * 32 + 8 * (j >> 2) + (j & 3)));
+    for (int g = 0; g < NKB * 4; ++g) alibi_u[g] = uniform_f(alibi_slope2 * (float)(8 * g));
   }
-  const float cap2 = a.softcap * kLog2e;            // softcap in log2 units
+  const float cap2 = a.softcap * kLog2e;  // softcap in log2 units
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
   // cap * log2e * tanh(raw * scale / cap) from exp2 and rcp
   auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap2); };
@@ -190,8 +194,10 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
   const int v_row0 = 4 * hh + (r16 >> 2);
   const int v_col0 = 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
 
-  auto tile = [&](auto full_c, int buf, int n0) {
-    constexpr bool FULL = decltype(full_c)::value;
+  // One KV tile for this wave.  Only the element mask depends on the tile
+  // class, and it edits the score registers in place, so the MFMA
+  // accumulators flow through a single path (no copies at a merge point).
+  auto tile = [&](bool full, int buf, int n0) {
     // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
     f32x16 s[NKB];
 #pragma unroll
@@ -202,19 +208,29 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
       for (int st = 0; st < NDS; ++st) s[kb] = mfma32(*(const bf16x8*)(krow + st * 16), qreg[st], s[kb]);
     }
 
-    // ---- score modifier, mask, tile row max
+    // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
     const int kbase = n0 + 4 * hh;
-    const float alibi_base = (SM == SM_ALIBI) ? alibi_slope2 * (float)(kbase - qi) : 0.f;
-    float tmax = neg_inf();
+    if constexpr (SM != SM_NONE) {
+      float ab[4];
+      if constexpr (SM == SM_ALIBI) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+        for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi + c);
+      }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-        float x = s[kb][j];
-        if constexpr (SM == SM_ALIBI) x = fmaf(x, a.c, alibi_k[kb * 16 + j]);
-        if constexpr (SM == SM_SOFTCAP && !FULL) x = softcap_t(x);
-        if constexpr (!FULL) {
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if constexpr (SM == SM_ALIBI) s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
+          else s[kb][j] = softcap_t(s[kb][j]);
+        }
+    }
+    // ---- element mask, partial tiles only (wave-uniform branch)
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
           bool ok = off < a.Skv - kbase;
           if constexpr (MK == MK_CAUSAL) {
             ok = ok && (off <= qi - kbase);
@@ -226,21 +242,22 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
           } else if constexpr (MK == MK_DOC) {
             ok = ok && (Ds[buf][off + 4 * hh] == dq);
           }
-          x = ok ? x : neg_inf();
+          s[kb][j] = ok ? s[kb][j] : neg_inf();
         }
-        s[kb][j] = x;
-        tmax = fmaxf(tmax, x);
       }
     }
-    float tile_max;  // log2 units
+    // ---- tile row max: four independent v_max3 chains, then the lane pair
+    float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) mx[(j >> 1) & 3] = fmaxf(mx[(j >> 1) & 3], fmaxf(s[kb][j], s[kb][j + 1]));
+    const float lmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+    float tile_max;  // log2 units, shared by lanes l and l^32
     if constexpr (SM == SM_NONE) {
-      tile_max = xhalf_max(tmax) * a.c;
-    } else if constexpr (SM == SM_ALIBI) {
-      tile_max = xhalf_max(tmax + alibi_base);
-    } else if constexpr (FULL) {
-      tile_max = xhalf_max(softcap_t(tmax));  // tanh is monotone: cap the raw max
+      tile_max = xhalf_max(lmax) * a.c;
     } else {
-      tile_max = xhalf_max(tmax);
+      tile_max = xhalf_max(lmax);
     }
 
     // ---- lazy rescale: raise the reference only when the max grew by > 2^kTau
@@ -257,8 +274,6 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
 
     // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
     bf16x8 pb[NPS];
-    const float mb = m_sub - alibi_base;       // ALiBi: fold the per-lane bias base into the reference
-    const float cm = cap2 - m_sub;             // softcap, full tiles
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -267,12 +282,6 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
         if constexpr (SM == SM_NONE) {
           p0 = exp2_fast(fmaf(s[kb][j], a.c, -m_sub));
           p1 = exp2_fast(fmaf(s[kb][j + 1], a.c, -m_sub));
-        } else if constexpr (SM == SM_ALIBI) {
-          p0 = exp2_fast(s[kb][j] - mb);
-          p1 = exp2_fast(s[kb][j + 1] - mb);
-        } else if constexpr (FULL) {
-          p0 = exp2_fast(fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(s[kb][j] * sc_k)), cm));
-          p1 = exp2_fast(fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(s[kb][j + 1] * sc_k)), cm));
         } else {
           p0 = exp2_fast(s[kb][j] - m_sub);
           p1 = exp2_fast(s[kb][j + 1] - m_sub);
@@ -325,10 +334,7 @@ __global__ __launch_bounds__(NT, min_waves<D>()) void attn_fwd_kernel(const Attn
       full &= (d0 == dqw) && (d1 == dqwlast) && (dqw == dqwlast);
     }
     if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
-    if (__builtin_amdgcn_readfirstlane((int)full))
-      tile(std::true_type{}, buf, n0);
-    else
-      tile(std::false_type{}, buf, n0);
+    tile(__builtin_amdgcn_readfirstlane((int)full) != 0, buf, n0);
   }
 
   // ---- epilogue: O / l, bf16 store, optional LSE

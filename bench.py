@@ -302,6 +302,36 @@ def run_sweep(path, steps, warmup):
     f.close()
 
 
+def run_profile(what, steps):
+    """Launch one kernel `steps` times with nothing else on the stream."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    if what == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
+        return
+    import attention_variants_amd as av
+
+    av.load_library()
+    B, H, S, D = 4, 16, 4096, 64
+    x = wi.attention_inputs(B, H, H, S, S, D)
+    q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        av.attn_fwd(q, k, v, score_mod=what, out=out)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": f"attn_fwd {what}", "B": B, "H": H, "S": S, "D": D, "launches": steps,
+                      "algorithmic_bytes_per_launch": attn_bytes(B, H, H, S, D)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -310,6 +340,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
+    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy"], default=None,
+                    help="launch only this kernel --steps times (for counter collection); 'copy' is a "
+                         "plain 1 GiB device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; --gpus must be 1 (no multi-GPU path exists)",
@@ -317,6 +350,9 @@ def main():
         sys.exit(2)
     if args.sweep:
         run_sweep(args.sweep, args.steps, args.warmup)
+        return
+    if args.profile:
+        run_profile(args.profile, args.steps)
         return
     rec = run_headline(args)
     print(json.dumps(rec), flush=True)
