@@ -43,7 +43,7 @@
 //    made XCD-aware); causal and PrefixLM grids start with the heaviest query
 //    tiles.
 
-#include "av_device.hpp"
+#include "attn_tile.hpp"
 #include "av_kernels.hpp"
 
 namespace av {
@@ -52,7 +52,6 @@ namespace {
 constexpr int BM = kAttnBM;  // query rows per workgroup
 constexpr int BN = 64;       // keys per KV tile
 constexpr int NT = 256;      // threads per workgroup
-constexpr float kTau = 8.f;  // lazy-rescale threshold, log2 units
 
 // Waves per SIMD each instantiation's register budget is sized for.  Four
 // (<= 128 VGPRs; the LDS of four 38 KB workgroups also fits a CU) where the
@@ -87,7 +86,10 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   const int L = xcd_remap(blockIdx.x, a.total);
   const int mt_lin = L % a.nM;
   const int bh = L / a.nM;
-  const int hq = bh % a.Hq, b = bh / a.Hq;
+  // Evoformer (pair bias shared over the batch): heads outermost, so one XCD's
+  // run of tiles covers few heads and their bias stays in its L2.
+  const int hq = (SM == SM_BIAS) ? bh / a.B : bh % a.Hq;
+  const int b = (SM == SM_BIAS) ? bh % a.B : bh / a.Hq;
   const int hk = hq / a.g;
   const int mt = (MK == MK_CAUSAL || MK == MK_PREFIX) ? (a.nM - 1 - mt_lin) : mt_lin;
   const int q0 = mt * BM;
@@ -137,9 +139,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   f32x16 o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  float m_ref = neg_inf();  // exponent reference (log2 units), identical in lanes l and l^32
-  float m_sub = 0.f;        // m_ref with -inf replaced by 0 (the value subtracted in exp2)
-  float l_run = 0.f;        // sum of this lane's bf16 probabilities, relative to m_ref
+  RowState st;
+  const VtLane vl(lane);
 
   // score-modifier constants
   // ALiBi, log2 units: bias(kb, j) = slope * (kj - qi) with kj = n0 + 4*hh + 32*kb + 8*(j/4) + j%4
@@ -152,6 +153,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < NKB * 4; ++g) alibi_u[g] = uniform_f(alibi_slope2 * (float)(8 * g));
   }
+  // Evoformer pair bias of head hq, rows qi: 4 keys (8 bytes) per load
+  const auto brs = make_rsrc(SM == SM_BIAS ? (const bf16*)a.bias + (size_t)hq * a.Sq * a.Skv : nullptr,
+                             SM == SM_BIAS ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
   const float cap2 = a.softcap * kLog2e;  // softcap in log2 units
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
   // cap * log2e * tanh(raw * scale / cap) from exp2 and rcp
@@ -189,27 +193,44 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
   };
 
-  // per-lane parts of the transposed V read: rows 4*hh + r/4 (+8), columns 16*g + 4*(r%4)
-  const int r16 = lane & 15;
-  const int v_row0 = 4 * hh + (r16 >> 2);
-  const int v_col0 = 16 * ((lane >> 4) & 1) + 4 * (r16 & 3);
-
   // One KV tile for this wave.  Only the element mask depends on the tile
   // class, and it edits the score registers in place, so the MFMA
   // accumulators flow through a single path (no copies at a merge point).
   auto tile = [&](bool full, int buf, int n0) {
+    const int kbase = n0 + 4 * hh;
+    // ---- pair bias loads issued ahead of the MFMAs: keys kbase + 32*kb + 8*g + 0..3
+    i32x4 braw[NKB * 2];
+    if constexpr (SM == SM_BIAS) {
+      const uint32_t rowoff = (uint32_t)(qi * a.Skv + kbase) * 2;
+      if (a.Skv % 4 == 0) {
+#pragma unroll
+        for (int g = 0; g < NKB * 4; g += 2) {
+          const auto lo = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16, 0, 0);
+          const auto hi = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16 + 16, 0, 0);
+          braw[g >> 1] = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+        }
+      } else {  // rows not 8-byte aligned: 16-bit loads
+#pragma unroll
+        for (int g = 0; g < NKB * 4; ++g) {
+          int w2[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const uint32_t o0 = rowoff + g * 16 + h2 * 4;
+            const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0, 0, 0);
+            const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0 + 2, 0, 0);
+            w2[h2] = (int)(x0 | (x1 << 16));
+          }
+          braw[g >> 1][(g & 1) * 2] = w2[0];
+          braw[g >> 1][(g & 1) * 2 + 1] = w2[1];
+        }
+      }
+    }
     // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
     f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const bf16* krow = &Ks[buf][(kb * 32 + l32) * KP + hh * 8];
-#pragma unroll
-      for (int st = 0; st < NDS; ++st) s[kb] = mfma32(*(const bf16x8*)(krow + st * 16), qreg[st], s[kb]);
-    }
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = qk_block<NDS, KP>(Ks[buf], kb, 0, qreg, l32, hh);
 
     // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
-    const int kbase = n0 + 4 * hh;
     if constexpr (SM != SM_NONE) {
       float ab[4];
       if constexpr (SM == SM_ALIBI) {
@@ -220,8 +241,15 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if constexpr (SM == SM_ALIBI) s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
-          else s[kb][j] = softcap_t(s[kb][j]);
+          if constexpr (SM == SM_ALIBI) {
+            s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
+          } else if constexpr (SM == SM_SOFTCAP) {
+            s[kb][j] = softcap_t(s[kb][j]);
+          } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
+            const int wd = braw[(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
+            const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
+            s[kb][j] = fmaf(s[kb][j], a.c, bv * kLog2e);
+          }
         }
     }
     // ---- element mask, partial tiles only (wave-uniform branch)
@@ -246,65 +274,19 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         }
       }
     }
-    // ---- tile row max: four independent v_max3 chains, then the lane pair
-    float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) mx[(j >> 1) & 3] = fmaxf(mx[(j >> 1) & 3], fmaxf(s[kb][j], s[kb][j + 1]));
-    const float lmax = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-    float tile_max;  // log2 units, shared by lanes l and l^32
-    if constexpr (SM == SM_NONE) {
-      tile_max = xhalf_max(lmax) * a.c;
-    } else {
-      tile_max = xhalf_max(lmax);
-    }
-
-    // ---- lazy rescale: raise the reference only when the max grew by > 2^kTau
-    if (any_lane(tile_max > m_ref + kTau)) {
-      const float m_new = fmaxf(m_ref, tile_max);
-      const float m_new_sub = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_ref - m_new_sub);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-      m_ref = m_new;
-      m_sub = m_new_sub;
-    }
+    // ---- tile row max (log2 units, shared by lanes l and l^32), lazy rescale
+    const float lmax = xhalf_max(block_max<NKB>(s));
+    st.update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o);
 
     // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
     bf16x8 pb[NPS];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        float p0, p1;
-        if constexpr (SM == SM_NONE) {
-          p0 = exp2_fast(fmaf(s[kb][j], a.c, -m_sub));
-          p1 = exp2_fast(fmaf(s[kb][j + 1], a.c, -m_sub));
-        } else {
-          p0 = exp2_fast(s[kb][j] - m_sub);
-          p1 = exp2_fast(s[kb][j + 1] - m_sub);
-        }
-        const bf16x2 pp = {(bf16)p0, (bf16)p1};
-        l_run = add_bf16_pair(pp, l_run);
-        pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
-        pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
-      }
-    }
+    exp_pack<NKB>(s, SM == SM_NONE ? a.c : 1.f, st, pb);
 
     // ---- O^T += V^T P^T, V^T operand via two transposed LDS reads per MFMA
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int t = 0; t < NPS; ++t) {
-        const bf16* vp = &Vs[buf][((t >> 1) * 32 + 16 * (t & 1) + v_row0) * VP + db * 32 + v_col0];
-        const i16x4 lo = lds_read_tr16(vp);
-        const i16x4 hi = lds_read_tr16(vp + 8 * VP);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[db] = mfma32(vf, pb[t], o[db]);
-      }
-    }
+      for (int t = 0; t < NPS; ++t) o[db] = mfma32(vt_operand<VP>(Vs[buf], t, db * 32, vl), pb[t], o[db]);
   };
 
   if (n_lo < n_hi) gload(n_lo);
@@ -338,9 +320,28 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   }
 
   // ---- epilogue: O / l, bf16 store, optional LSE
-  const float l_tot = xhalf_sum(l_run);
+  const float l_tot = xhalf_sum(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < a.Sq) {
+  if (qi < a.Sq && SM == SM_BIAS) {
+    // Evoformer: out[b, qi, hq*D + d] = sigmoid(gate[b, hq, qi, d]) * O[d] / l
+    bf16* orow = (bf16*)a.o + ((size_t)b * a.Sq + qi) * (size_t)(a.Hq * D) + (size_t)hq * D;
+    const bf16* grow = (const bf16*)a.gate + qoff + (size_t)qi * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * hh;
+        const bf16x4 gv = *(const bf16x4*)(grow + d0);
+        bf16x4 val;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sig = rcp_fast(1.f + exp2_fast(-(float)gv[e] * kLog2e));
+          val[e] = (bf16)(o[db][g4 * 4 + e] * inv * sig);
+        }
+        *(bf16x4*)(orow + d0) = val;
+      }
+    }
+  } else if (qi < a.Sq) {
     bf16* orow = (bf16*)a.o + qoff + (size_t)qi * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
     }
     if (a.lse != nullptr && hh == 0) {
-      a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
+      a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi] = l_tot > 0.f ? (st.m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
     }
   }
 }
@@ -387,6 +388,8 @@ hipError_t launch_sm(const AttnArgs& a, int sm, int mask, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_evo_attention(const AttnArgs& a, hipStream_t stream) { return launch_one<32, SM_BIAS, MK_NONE>(a, stream); }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream) {
   switch (D) {

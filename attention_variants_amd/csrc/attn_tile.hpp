@@ -1,0 +1,114 @@
+// Tile-level building blocks shared by the attention kernels (fused
+// attention, differential attention, Evoformer gated attention).
+//
+// Layout conventions (one wave, 32 query rows; lane l = 32*hh + l32):
+//  * S^T block = K_blk (32 keys x d) . Q^T (d x 32 queries), 32x32x16 bf16
+//    MFMA.  Lane l holds query l32 and keys 8*(j/4) + 4*hh + j%4, j = 0..15,
+//    of the 32-key block: one query per lane pair, so row reductions are
+//    in-register plus one cross-half swap.
+//  * O^T block = V^T (32 d x keys) . P^T (keys x 32 queries).  The P^T
+//    operand of k-step t (16 keys) is registers j = 8*(t%2) .. +7 of S^T
+//    block t/2 converted to bf16; the matching V^T operand is read from a
+//    row-major V tile with two transposed LDS reads.
+//  * Scores are in log2 units; the exponent reference m_ref is raised only
+//    when a tile max exceeds it by more than 2^kLazyTau.
+#pragma once
+
+#include "av_device.hpp"
+
+namespace av {
+
+constexpr float kLazyTau = 8.f;
+
+// S^T for key block kb of an LDS K tile (row pitch KP elements), over NSTEP
+// k-steps of 16 starting at column c0.
+template <int NSTEP, int KP>
+__device__ __forceinline__ f32x16 qk_block(const bf16* Ks, int kb, int c0, const bf16x8* qreg, int l32, int hh) {
+  f32x16 s = {};
+  const bf16* krow = Ks + (kb * 32 + l32) * KP + c0 + hh * 8;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st) s = mfma32(*(const bf16x8*)(krow + st * 16), qreg[st], s);
+  return s;
+}
+
+// Per-lane parts of the transposed V read: rows 4*hh + r/4 (+8), columns 16*g + 4*(r%4).
+struct VtLane {
+  int row0, col0;
+  __device__ __forceinline__ explicit VtLane(int lane)
+      : row0(4 * (lane >> 5) + ((lane & 15) >> 2)), col0(16 * ((lane >> 4) & 1) + 4 * (lane & 3)) {}
+};
+
+// V^T operand (32 d-columns starting at dcol x 16 keys) of PV k-step t, from
+// an LDS V tile with row pitch VP elements.
+template <int VP>
+__device__ __forceinline__ bf16x8 vt_operand(const bf16* Vs, int t, int dcol, const VtLane& vl) {
+  const bf16* vp = Vs + ((t >> 1) * 32 + 16 * (t & 1) + vl.row0) * VP + dcol + vl.col0;
+  const i16x4 lo = lds_read_tr16(vp);
+  const i16x4 hi = lds_read_tr16(vp + 8 * VP);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// In-place element mask of one S^T block: keep[off] decides, off = key offset
+// of the register inside the 32-key block.
+template <typename Keep>
+__device__ __forceinline__ void mask_block(f32x16& s, Keep keep) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int off = 8 * (j >> 2) + (j & 3);
+    s[j] = keep(off) ? s[j] : neg_inf();
+  }
+}
+
+// Max over the registers of NB S^T blocks (four independent chains).
+template <int NB>
+__device__ __forceinline__ float block_max(const f32x16* s) {
+  float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) mx[(j >> 1) & 3] = fmaxf(mx[(j >> 1) & 3], fmaxf(s[kb][j], s[kb][j + 1]));
+  return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+}
+
+// Online-softmax state of one query row held by a lane pair.
+struct RowState {
+  float m_ref = neg_inf();  // exponent reference (log2 units), equal in lanes l and l^32
+  float m_sub = 0.f;        // m_ref with -inf replaced by 0
+  float l = 0.f;            // this lane's share of the row sum, relative to m_ref
+
+  // Raise the reference if any lane's tile max exceeds it by more than
+  // 2^kLazyTau; rescale l and the NO accumulators by the same factor.
+  template <int NO>
+  __device__ __forceinline__ void update(float tile_max, f32x16* o) {
+    if (any_lane(tile_max > m_ref + kLazyTau)) {
+      const float m_new = fmaxf(m_ref, tile_max);
+      const float m_new_sub = (m_new == neg_inf()) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_ref - m_new_sub);
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < NO; ++i) o[i] *= alpha;
+      m_ref = m_new;
+      m_sub = m_new_sub;
+    }
+  }
+};
+
+// p = exp2(s * c - m_sub) for the registers of NB S^T blocks, packed to bf16
+// P^T operands pb[2*NB]; adds the bf16 values to the lane's row sum.
+template <int NB>
+__device__ __forceinline__ void exp_pack(const f32x16* s, float c, RowState& st, bf16x8* pb) {
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = exp2_fast(fmaf(s[kb][j], c, -st.m_sub));
+      const float p1 = exp2_fast(fmaf(s[kb][j + 1], c, -st.m_sub));
+      const bf16x2 pp = {(bf16)p0, (bf16)p1};
+      st.l = add_bf16_pair(pp, st.l);
+      pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
+      pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+    }
+  }
+}
+
+}  // namespace av

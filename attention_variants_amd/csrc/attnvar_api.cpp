@@ -139,7 +139,7 @@ int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, cons
       out == nullptr)
     return AV_ERR_NULL;
   if (Ns <= 0 || Nr <= 0 || Cm <= 0 || H <= 0 || dh <= 0) return AV_ERR_SHAPE;
-  if (dh != 32 || Cm % 64 != 0 || (H * dh) % 64 != 0) return AV_ERR_UNSUPPORTED;
+  if (dh != 32 || Cm % 64 != 0 || (H * dh) % 128 != 0) return AV_ERR_UNSUPPORTED;
   if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
   if (!aligned(m, 16) || !aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(wg, 16) ||
       !aligned(bias, 16) || !aligned(out, 16))

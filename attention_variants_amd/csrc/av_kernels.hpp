@@ -7,7 +7,9 @@
 
 namespace av {
 
-enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2 };
+// SM_BIAS (internal): Evoformer pair bias added to the scaled score, with the
+// sigmoid-gate epilogue and a token-major [B, Sq, Hq*D] output.
+enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3 };
 enum MaskKind : int { MK_NONE = 0, MK_CAUSAL = 1, MK_WINDOW = 2, MK_PREFIX = 3, MK_DOC = 4 };
 
 // Kernel argument block of the fused attention forward (passed by value).
@@ -18,6 +20,8 @@ struct AttnArgs {
   void* o;
   float* lse;        // nullable
   const int* doc;    // MK_DOC only
+  const void* bias;  // SM_BIAS: [Hq, Sq, Skv] bf16 pair bias, shared over the batch
+  const void* gate;  // SM_BIAS: [B, Hq, Sq, D] bf16 gate pre-activations (same layout as q)
   int B, Hq, Hkv, Sq, Skv;
   int g;             // Hq / Hkv
   int nM;            // query tiles per (b, head)
@@ -34,6 +38,8 @@ struct AttnArgs {
 constexpr int kAttnBM = 128;
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
+// Evoformer gated attention over the projected workspace (D = 32, SM_BIAS).
+hipError_t launch_evo_attention(const AttnArgs& a, hipStream_t stream);
 
 struct DiffArgs {
   const void* q;

@@ -1,6 +1,171 @@
-#include "av_device.hpp"
+// Evoformer row-wise gated self-attention with pair bias, gfx950.
+//
+// The pages name this variant among those Flashlight fuses and templates
+// cannot express (talk notes "Flashlight: PyTorch Compiler Extensions to
+// Accelerate Attention Variants", "Evaluation: complex attention variants"
+// and the AlphaFold2 end-to-end section: 8 heads x 32) but print no formula.
+// Reading implemented, per MSA sequence s and head h:
+//   q, k, v, g = m Wq, m Wk, m Wv, m Wg
+//   out[s, i, h*dh + e] = sigmoid(g[s, i, h*dh + e]) * softmax_j(q_i.k_j * scale + bias[h, i, j]) v_j[e]
+//
+// Two launches:
+//  1. evo_proj_kernel: the four projections as one bf16 MFMA GEMM with fp32
+//     accumulation (the pages' precision rule), M = Ns*Nr tokens, N = 4*H*dh
+//     channels, K = Cm.  It computes C^T = W^T m^T so that each lane ends up
+//     holding 4 consecutive channels of one token; results are rounded to
+//     bf16 and scattered head-major into the workspace as four planes
+//     [Ns, H, Nr, dh] (q, k, v, g).
+//  2. the fused attention kernel at D = dh = 32 with the pair bias as score
+//     modifier and the sigmoid gate + token-major store as epilogue; each
+//     (sequence, head, 128-residue tile) is one workgroup, sequences vary
+//     fastest within a head so bias[h] stays resident in L2.
+
+#include "attn_tile.hpp"
 #include "av_kernels.hpp"
+
 namespace av {
-size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
-hipError_t launch_evoformer(const EvoArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int GM = 128;  // tokens per workgroup
+constexpr int GN = 128;  // output channels per workgroup
+constexpr int GK = 64;   // K chunk staged in LDS
+constexpr int NT = 256;
+constexpr int MP = GK + 8;   // m tile pitch: 8 rows -> 8 distinct 16-byte bank groups
+constexpr int WP = GN + 16;  // W tile pitch: 4 rows -> 4 distinct 32-byte bank groups
+
+__global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 Ms[2][GM * MP];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][GK * WP];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int HD = a.H * a.dh;            // channels per projection
+  const int N = 4 * HD;
+  const int M = a.Ns * a.Nr;
+  const int ntiles = N / GN;
+  const int total = ((M + GM - 1) / GM) * ntiles;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int mt = L / ntiles, nt = L % ntiles;  // the channel tiles of one token tile are neighbours
+  const int n0 = nt * GN;
+  const int p = n0 / HD;                       // projection of this tile (GN divides HD)
+  const int c0 = n0 % HD;
+  const int wn = w & 1, wm = w >> 1;           // wave: 64 channels x 64 tokens
+
+  const auto mrs = make_rsrc((const bf16*)a.m + (size_t)mt * GM * a.Cm, (uint32_t)min(GM, M - mt * GM) * a.Cm * 2);
+  const bf16* wbase = (const bf16*)a.w[p];
+  const auto wrs = make_rsrc(wbase, (uint32_t)a.Cm * HD * 2);
+
+  // staging: m chunk 128 x 64 and W chunk 64 x 128, 4 x 16 bytes per thread each
+  i32x4 mr[4], wr[4];
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + NT * c;
+      const int mrow = idx >> 3, mcol = idx & 7;
+      mr[c] = buf_load16(mrs, (uint32_t)(mrow * a.Cm + kc * GK + mcol * 8) * 2);
+      const int wrow = idx >> 4, wcol = idx & 15;
+      wr[c] = buf_load16(wrs, (uint32_t)((kc * GK + wrow) * HD + c0 + wcol * 8) * 2);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + NT * c;
+      *(i32x4*)&Ms[buf][(idx >> 3) * MP + (idx & 7) * 8] = mr[c];
+      *(i32x4*)&Ws[buf][(idx >> 4) * WP + (idx & 15) * 8] = wr[c];
+    }
+  };
+
+  // W^T operand by transposed reads: lane (channel n, half hh) needs W[k0 + 8*hh + 0..7][n];
+  // lane r of each 16-lane group points at row k0 + 8*hh + r/4 (+4), columns 16*g + 4*(r%4).
+  const int wr_row = 8 * hh + ((lane & 15) >> 2);
+  const int wr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+
+  const int nkc = a.Cm / GK;
+  gload(0);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    sstore(buf);
+    __syncthreads();
+    if (kc + 1 < nkc) gload(kc + 1);
+#pragma unroll
+    for (int ks = 0; ks < GK / 16; ++ks) {
+      bf16x8 wa[2], mb[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bf16* wp = &Ws[buf][(ks * 16 + wr_row) * WP + wn * 64 + nb * 32 + wr_col];
+        const i16x4 lo = lds_read_tr16(wp);
+        const i16x4 hi = lds_read_tr16(wp + 4 * WP);
+        wa[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mb2 = 0; mb2 < 2; ++mb2) mb[mb2] = *(const bf16x8*)&Ms[buf][(wm * 64 + mb2 * 32 + l32) * MP + ks * 16 + hh * 8];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int mb2 = 0; mb2 < 2; ++mb2) acc[nb][mb2] = mfma32(wa[nb], mb[mb2], acc[nb][mb2]);
+    }
+  }
+
+  // C^T block: lane holds token l32 of the block, channels 8*(j/4) + 4*hh + j%4
+  const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
+  bf16* out = (bf16*)a.ws + (size_t)p * plane;
+#pragma unroll
+  for (int mb2 = 0; mb2 < 2; ++mb2) {
+    const int tok = mt * GM + wm * 64 + mb2 * 32 + l32;
+    if (tok >= M) continue;
+    const int sq = tok / a.Nr, ri = tok % a.Nr;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ch = c0 + wn * 64 + nb * 32 + 8 * g4 + 4 * hh;  // channel within the projection
+        const int h = ch / a.dh, e = ch % a.dh;
+        bf16x4 val;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) val[q] = (bf16)acc[nb][mb2][g4 * 4 + q];
+        *(bf16x4*)(out + (((size_t)sq * a.H + h) * a.Nr + ri) * a.dh + e) = val;
+      }
+    }
+  }
 }
+
+}  // namespace
+
+size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
+
+hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
+  const int M = a.Ns * a.Nr, N = 4 * a.H * a.dh;
+  const int gemm_blocks = ((M + GM - 1) / GM) * (N / GN);
+  hipLaunchKernelGGL(evo_proj_kernel, dim3(gemm_blocks), dim3(NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
+  const bf16* ws = (const bf16*)a.ws;
+  AttnArgs t{};
+  t.q = ws;
+  t.k = ws + plane;
+  t.v = ws + 2 * plane;
+  t.gate = ws + 3 * plane;
+  t.o = a.out;
+  t.lse = nullptr;
+  t.doc = nullptr;
+  t.bias = a.bias;
+  t.B = a.Ns;
+  t.Hq = t.Hkv = a.H;
+  t.Sq = t.Skv = a.Nr;
+  t.g = 1;
+  t.nM = (a.Nr + kAttnBM - 1) / kAttnBM;
+  t.total = a.Ns * a.H * t.nM;
+  t.c = a.c;
+  t.scale = a.c / 1.4426950408889634f;
+  t.softcap = 1.f;
+  return launch_evo_attention(t, stream);
+}
+
+}  // namespace av

@@ -127,7 +127,7 @@ int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
  * The projections are computed into `workspace` (bf16, owned by the caller,
  * at least evoformer_workspace_bytes(...) bytes, 256-byte aligned) by one
  * kernel, then consumed by the attention kernel.  scale = 0 selects
- * 1/sqrt(dh).  Supported: dh = 32, Cm a multiple of 64, H*dh a multiple of 64. */
+ * 1/sqrt(dh).  Supported: dh = 32, Cm a multiple of 64, H*dh a multiple of 128. */
 size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh);
 int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
                              const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns,

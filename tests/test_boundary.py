@@ -117,7 +117,7 @@ def test_evoformer_rejections(lib):
     assert need == 4 * 128 * 256 * 8 * 32 * 2
     assert lib.evoformer_workspace_bytes(0, 256, 8, 32) == 0
 
-    def call(m=P, w=P2, bias=P3, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=2, dh=32, scale=0.0):
+    def call(m=P, w=P2, bias=P3, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):
         if wsb is None:
             wsb = lib.evoformer_workspace_bytes(max(Ns, 1), max(Nr, 1), max(H, 1), max(dh, 1))
         return lib.evoformer_gated_attn_fwd(m, w, w, w, w, bias, out, ws, wsb, Ns, Nr, Cm, H, dh, scale, None)
@@ -128,6 +128,7 @@ def test_evoformer_rejections(lib):
     assert call(Ns=0) == -2
     assert call(dh=64) == -3
     assert call(Cm=48) == -3
+    assert call(H=2) == -3  # H*dh must be a multiple of 128
     assert call(scale=float("nan")) == -7
     assert call(m=P + 2) == -4
     assert call(ws=None) == -5
