@@ -36,7 +36,11 @@ from workloads import inputs as wi  # noqa: E402
 METRIC = "attention fwd TFLOP/s (visible FLOPs) & % bf16 MFMA peak, per variant"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("attention_variants_amd/csrc/attn_fwd.hip", "attention_variants_amd/csrc/av_device.hpp")
+KERNEL_SOURCES = (
+    "attention_variants_amd/csrc/attn_fwd.hip",
+    "attention_variants_amd/csrc/attn_tile.hpp",
+    "attention_variants_amd/csrc/av_device.hpp",
+)
 
 
 # ----------------------------------------------------------------- work model
