@@ -59,7 +59,11 @@ constexpr int NT = 256;      // threads per workgroup
 template <int D, int SM, int MK>
 constexpr int min_waves() {
   if (D <= 32) return 4;
-  if (D == 64) return (SM == SM_NONE && (MK == MK_NONE || MK == MK_CAUSAL || MK == MK_WINDOW)) ? 4 : 3;
+  if (D == 64)
+    return ((SM == SM_NONE && (MK == MK_NONE || MK == MK_CAUSAL || MK == MK_WINDOW)) ||
+            (SM == SM_SOFTCAP_FIXED && MK == MK_NONE))
+               ? 4
+               : 3;
   return 2;
 }
 
@@ -140,6 +144,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   RowState st;
+  if constexpr (SM == SM_SOFTCAP_FIXED) st.m_ref = a.softcap * kLog2e;  // the scores hold t - m_ref already
   const VtLane vl(lane);
 
   // score-modifier constants
@@ -158,8 +163,10 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
                              SM == SM_BIAS ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
   const float cap2 = a.softcap * kLog2e;  // softcap in log2 units
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
-  // cap * log2e * tanh(raw * scale / cap) from exp2 and rcp
-  auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap2); };
+  // cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k)), from exp2 and rcp;
+  // with the fixed reference the kernel keeps t - cap2 (one op less)
+  const float cap_off = SM == SM_SOFTCAP_FIXED ? 0.f : cap2;
+  auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap_off); };
 
   i32x4 kr[NCH], vr[NCH];
   int dr = 0;
@@ -225,62 +232,67 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         }
       }
     }
-    // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = qk_block<NDS, KP>(Ks[buf], kb, 0, qreg, l32, hh);
-
-    // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
-    if constexpr (SM != SM_NONE) {
-      float ab[4];
-      if constexpr (SM == SM_ALIBI) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi + c);
-      }
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if constexpr (SM == SM_ALIBI) {
-            s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
-          } else if constexpr (SM == SM_SOFTCAP) {
-            s[kb][j] = softcap_t(s[kb][j]);
-          } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
-            const int wd = braw[(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
-            const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
-            s[kb][j] = fmaf(s[kb][j], a.c, bv * kLog2e);
-          }
-        }
-    }
-    // ---- element mask, partial tiles only (wave-uniform branch)
-    if (!full) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-          bool ok = off < a.Skv - kbase;
-          if constexpr (MK == MK_CAUSAL) {
-            ok = ok && (off <= qi - kbase);
-          } else if constexpr (MK == MK_WINDOW) {
-            const int rel = qi - kbase;
-            ok = ok && (off <= rel) && (off > rel - a.window);
-          } else if constexpr (MK == MK_PREFIX) {
-            ok = ok && ((off < a.prefix - kbase) || (off <= qi - kbase));
-          } else if constexpr (MK == MK_DOC) {
-            ok = ok && (Ds[buf][off + 4 * hh] == dq);
-          }
-          s[kb][j] = ok ? s[kb][j] : neg_inf();
-        }
-      }
-    }
-    // ---- tile row max (log2 units, shared by lanes l and l^32), lazy rescale
-    const float lmax = xhalf_max(block_max<NKB>(s));
-    st.update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o);
-
-    // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
+    // Exponent reference: a softcap with a small cap has bounded scores, so
+    // its reference sits at the cap and no max is taken; every other variant
+    // tracks the tile max with the lazy rescale.
+    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
     bf16x8 pb[NPS];
-    exp_pack<NKB>(s, SM == SM_NONE ? a.c : 1.f, st, pb);
+    {
+      // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = qk_block<NDS, KP>(Ks[buf], kb, 0, qreg, l32, hh);
+
+      // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
+      if constexpr (SM != SM_NONE) {
+        float ab[4];
+        if constexpr (SM == SM_ALIBI) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi + c);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if constexpr (SM == SM_ALIBI) {
+              s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
+            } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+              s[kb][j] = softcap_t(s[kb][j]);
+            } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
+              const int wd = braw[(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
+              const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
+              s[kb][j] = fmaf(s[kb][j], a.c, bv * kLog2e);
+            }
+          }
+      }
+      // ---- element mask, partial tiles only (wave-uniform branch)
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+            bool ok = off < a.Skv - kbase;
+            if constexpr (MK == MK_CAUSAL) {
+              ok = ok && (off <= qi - kbase);
+            } else if constexpr (MK == MK_WINDOW) {
+              const int rel = qi - kbase;
+              ok = ok && (off <= rel) && (off > rel - a.window);
+            } else if constexpr (MK == MK_PREFIX) {
+              ok = ok && ((off < a.prefix - kbase) || (off <= qi - kbase));
+            } else if constexpr (MK == MK_DOC) {
+              ok = ok && (Ds[buf][off + 4 * hh] == dq);
+            }
+            s[kb][j] = ok ? s[kb][j] : neg_inf();
+          }
+        }
+      }
+      if constexpr (SM != SM_SOFTCAP_FIXED) {
+        const float lmax = xhalf_max(block_max<NKB>(s));
+        st.update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o);
+      }
+      st.l += exp_pack_sum<NKB, MODE>(s, a.c, st.m_sub, pb);
+    }
 
     // ---- O^T += V^T P^T, V^T operand via two transposed LDS reads per MFMA
 #pragma unroll
@@ -382,7 +394,8 @@ hipError_t launch_sm(const AttnArgs& a, int sm, int mask, hipStream_t stream) {
   switch (sm) {
     case SM_NONE: return launch_mask<D, SM_NONE>(a, mask, stream);
     case SM_ALIBI: return launch_mask<D, SM_ALIBI>(a, mask, stream);
-    case SM_SOFTCAP: return launch_mask<D, SM_SOFTCAP>(a, mask, stream);
+    case SM_SOFTCAP:
+      return a.fixed_ref ? launch_mask<D, SM_SOFTCAP_FIXED>(a, mask, stream) : launch_mask<D, SM_SOFTCAP>(a, mask, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -70,28 +70,60 @@ __device__ __forceinline__ float block_max(const f32x16* s) {
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
-// Online-softmax state of one query row held by a lane pair.
+// Online-softmax state of one query row held by a lane pair.  The reference
+// m_ref only has to keep the exponentials representable: the softmax is
+// exp(x - m) / sum exp(x - m) for ANY common m.
 struct RowState {
   float m_ref = neg_inf();  // exponent reference (log2 units), equal in lanes l and l^32
   float m_sub = 0.f;        // m_ref with -inf replaced by 0
   float l = 0.f;            // this lane's share of the row sum, relative to m_ref
 
-  // Raise the reference if any lane's tile max exceeds it by more than
-  // 2^kLazyTau; rescale l and the NO accumulators by the same factor.
+  // Raise the reference to the tile max where it is higher; rescale l and the
+  // NO accumulators by the same factor.
+  template <int NO>
+  __device__ __forceinline__ void raise(float tile_max, f32x16* o) {
+    const float m_new = fmaxf(m_ref, tile_max);
+    const float m_new_sub = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = exp2_fast(m_ref - m_new_sub);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < NO; ++i) o[i] *= alpha;
+    m_ref = m_new;
+    m_sub = m_new_sub;
+  }
+  // Lazy variant: only when some lane's tile max exceeds m_ref by > 2^kLazyTau.
   template <int NO>
   __device__ __forceinline__ void update(float tile_max, f32x16* o) {
-    if (any_lane(tile_max > m_ref + kLazyTau)) {
-      const float m_new = fmaxf(m_ref, tile_max);
-      const float m_new_sub = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_ref - m_new_sub);
-      l *= alpha;
-#pragma unroll
-      for (int i = 0; i < NO; ++i) o[i] *= alpha;
-      m_ref = m_new;
-      m_sub = m_new_sub;
-    }
+    if (any_lane(tile_max > m_ref + kLazyTau)) raise<NO>(tile_max, o);
   }
 };
+
+// p = exp2(s * c - m_sub) (MODE 0), exp2(s - m_sub) (MODE 1) or exp2(s)
+// (MODE 2) for the registers of NB S^T blocks, packed to bf16 P^T operands
+// pb[2*NB]; returns this lane's sum of the bf16 values.
+template <int NB, int MODE>
+__device__ __forceinline__ float exp_pack_sum(const f32x16* s, float c, float m_sub, bf16x8* pb) {
+  float acc = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      float x0 = s[kb][j], x1 = s[kb][j + 1];
+      if constexpr (MODE == 0) {
+        x0 = fmaf(x0, c, -m_sub);
+        x1 = fmaf(x1, c, -m_sub);
+      } else if constexpr (MODE == 1) {
+        x0 -= m_sub;
+        x1 -= m_sub;
+      }
+      const bf16x2 pp = {(bf16)exp2_fast(x0), (bf16)exp2_fast(x1)};
+      acc = add_bf16_pair(pp, acc);
+      pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
+      pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
+    }
+  }
+  return acc;
+}
 
 // p = exp2(s * c - m_sub) for the registers of NB S^T blocks, packed to bf16
 // P^T operands pb[2*NB]; adds the bf16 values to the lane's row sum.

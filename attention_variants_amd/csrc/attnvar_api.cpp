@@ -93,6 +93,9 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
   a.window = var->window;
   a.prefix = var->prefix_len;
+  // softcapped scores lie in [-cap, cap]: with the reference at +cap every
+  // exponential is in [2^(-2 cap log2 e), 1], far from fp32 underflow when <= 96
+  a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
   return hip_status(av::launch_attn_fwd(a, D, var->score_mod, var->mask, stream));
 }
 

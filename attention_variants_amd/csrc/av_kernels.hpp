@@ -7,9 +7,11 @@
 
 namespace av {
 
-// SM_BIAS (internal): Evoformer pair bias added to the scaled score, with the
-// sigmoid-gate epilogue and a token-major [B, Sq, Hq*D] output.
-enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3 };
+// Internal score modifiers: SM_BIAS = Evoformer pair bias added to the scaled
+// score, with the sigmoid-gate epilogue and a token-major [B, Sq, Hq*D]
+// output; SM_SOFTCAP_FIXED = softcap whose exponent reference is fixed at the
+// cap (chosen by the launcher when fixed_ref is set).
+enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3, SM_SOFTCAP_FIXED = 4 };
 enum MaskKind : int { MK_NONE = 0, MK_CAUSAL = 1, MK_WINDOW = 2, MK_PREFIX = 3, MK_DOC = 4 };
 
 // Kernel argument block of the fused attention forward (passed by value).
@@ -32,6 +34,7 @@ struct AttnArgs {
   float softcap;
   int window;
   int prefix;
+  int fixed_ref;     // softcap with 2 * cap * log2(e) <= 96: exponent reference fixed at the cap
 };
 
 // Query rows per workgroup of the attention forward kernel.

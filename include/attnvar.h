@@ -94,8 +94,8 @@ typedef struct {
  *   lse [B, Hq,  Sq]  fp32  natural-log sum-exp of the modified, masked
  *                           scores per row; may be NULL (not written).  The
  *                           row sum adds the bf16-rounded probabilities that
- *                           the PV product consumes, so lse is within about
- *                           2e-3 of the exact value (ln(1 + 2^-9)).
+ *                           the PV product consumes, so lse is within
+ *                           ln(1 + 2^-8) = 3.9e-3 of the exact value.
  * Query head h reads key/value head h / (Hq / Hkv).  D in {32, 64, 128}.
  * Sq == 0 launches nothing; Skv == 0 writes zero rows and lse = -inf.
  * Pointers of empty tensors may be NULL (q/out when Sq == 0, k/v when Skv == 0).
