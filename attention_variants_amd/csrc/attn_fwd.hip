@@ -19,10 +19,11 @@
 //    reduction plus one v_permlane32_swap, and the exponentiated tile feeds
 //    the second MFMA (O^T = V^T P^T) straight from registers as its B
 //    operand: no LDS round trip for P.
-//  * K and V tiles sit row-major in LDS (padded pitches, conflict-free for
-//    the read patterns below), double-buffered, with the next tile's global
-//    loads in flight while the current one is computed.  The V^T operand is
-//    read with gfx950's transposed LDS read, two per MFMA.
+//  * K and V tiles sit row-major in LDS, double-buffered, with the next
+//    tile's global loads in flight while the current one is computed.  K has
+//    a padded pitch (conflict-free 16-byte reads); V is XOR-swizzled in
+//    64-byte segments (conflict-free transposed reads, no padding).  The V^T
+//    operand is read with gfx950's transposed LDS read, two per MFMA.
 //  * Scores are carried in log2 units (scale * log2 e folded in); exp2 is the
 //    hardware v_exp_f32; accumulation is fp32 (talk notes, "Implementation
 //    details", precision item).
@@ -76,11 +77,10 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   constexpr int NCH = BN * CPR / NT; // chunks per thread per tensor
   constexpr int KP = D + 8;          // K row pitch (elements): 8 rows hit 8 distinct 16-byte bank groups
-  constexpr int VP = D + 16;         // V row pitch: 4 rows hit 4 distinct 32-byte bank groups
   static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * VP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];  // swizzled for transposed reads
   __shared__ __attribute__((aligned(16))) int Ds[2][MK == MK_DOC ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
   RowState st;
   if constexpr (SM == SM_SOFTCAP_FIXED) st.m_ref = a.softcap * kLog2e;  // the scores hold t - m_ref already
-  const VtLane vl(lane);
+  const TrLane<D> vl(lane);
 
   // score-modifier constants
   // ALiBi, log2 units: bias(kb, j) = slope * (kj - qi) with kj = n0 + 4*hh + 32*kb + 8*(j/4) + j%4
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       const int idx = tid + NT * c;
       const int row = idx / CPR, col = idx % CPR;
       *(i32x4*)&Ks[buf][row * KP + col * 8] = kr[c];
-      *(i32x4*)&Vs[buf][row * VP + col * 8] = vr[c];
+      *(i32x4*)&Vs[buf][tr_tile_off<D>(row, col * 8)] = vr[c];
     }
     if constexpr (MK == MK_DOC) {
       if (tid < BN) Ds[buf][tid] = dr;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int t = 0; t < NPS; ++t) o[db] = mfma32(vt_operand<VP>(Vs[buf], t, db * 32, vl), pb[t], o[db]);
+      for (int t = 0; t < NPS; ++t) o[db] = mfma32(vt_operand<D>(Vs[buf], t, db * 32, vl), pb[t], o[db]);
   };
 
   if (n_lo < n_hi) gload(n_lo);

@@ -31,20 +31,42 @@ __device__ __forceinline__ f32x16 qk_block(const bf16* Ks, int kb, int c0, const
   return s;
 }
 
-// Per-lane parts of the transposed V read: rows 4*hh + r/4 (+8), columns 16*g + 4*(r%4).
-struct VtLane {
-  int row0, col0;
-  __device__ __forceinline__ explicit VtLane(int lane)
-      : row0(4 * (lane >> 5) + ((lane & 15) >> 2)), col0(16 * ((lane >> 4) & 1) + 4 * (lane & 3)) {}
+// Row-major LDS tile read by transposed reads (V, or W of the projection
+// GEMM): W elements per row, no padding.  A transposed read serves 32 lanes
+// per pass from 4 consecutive rows (4*q .. 4*q+3) and 32 columns (64 bytes)
+// of each; the LDS bank window is 256 bytes, so those 4 row pieces must land
+// in 4 distinct 64-byte segments.  Rows of 128 or 256 bytes alone would
+// collide, so the 64-byte segments of each row are XOR-swizzled by a function
+// of (row mod 4): element column c of row r lives at c ^ (tr_swz<W>(r) * 32).
+template <int W>
+__device__ __forceinline__ constexpr int tr_swz(int row) {
+  return W == 64 ? ((row >> 1) & 1) : W == 128 ? (row & 3) : 0;  // W = 32: rows already 64 bytes apart
+}
+// Element offset of the 8-element (16-byte) chunk starting at column c (c % 8 == 0).
+template <int W>
+__device__ __forceinline__ int tr_tile_off(int row, int c) {
+  return row * W + (c ^ (tr_swz<W>(row) << 5));
+}
+
+// Per-lane parts of the transposed read: rows 4*hh + r/4 (+8), columns
+// 16*g + 4*(r%4) of the 32-column block; the swizzle depends only on the
+// lane, because every row this lane reads is congruent to 4*hh + r/4 mod 4.
+template <int W>
+struct TrLane {
+  int row0, col0, xo;
+  __device__ __forceinline__ explicit TrLane(int lane)
+      : row0(4 * (lane >> 5) + ((lane & 15) >> 2)),
+        col0(16 * ((lane >> 4) & 1) + 4 * (lane & 3)),
+        xo(tr_swz<W>((lane & 15) >> 2) << 5) {}
 };
 
 // V^T operand (32 d-columns starting at dcol x 16 keys) of PV k-step t, from
-// an LDS V tile with row pitch VP elements.
-template <int VP>
-__device__ __forceinline__ bf16x8 vt_operand(const bf16* Vs, int t, int dcol, const VtLane& vl) {
-  const bf16* vp = Vs + ((t >> 1) * 32 + 16 * (t & 1) + vl.row0) * VP + dcol + vl.col0;
+// a swizzled row-major LDS V tile of W columns.
+template <int W>
+__device__ __forceinline__ bf16x8 vt_operand(const bf16* Vs, int t, int dcol, const TrLane<W>& vl) {
+  const bf16* vp = Vs + ((t >> 1) * 32 + 16 * (t & 1) + vl.row0) * W + ((dcol + vl.col0) ^ vl.xo);
   const i16x4 lo = lds_read_tr16(vp);
-  const i16x4 hi = lds_read_tr16(vp + 8 * VP);
+  const i16x4 hi = lds_read_tr16(vp + 8 * W);
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 

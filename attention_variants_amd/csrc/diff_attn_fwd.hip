@@ -33,13 +33,12 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
   constexpr int NDB = DV / 32;          // O^T d-blocks per branch
   constexpr int NPS = BN / 16;          // PV k-steps
   constexpr int KP = DQ + 8;
-  constexpr int VP = DV + 16;
   constexpr int KCPR = DQ / 8, VCPR = DV / 8;
   constexpr int KCH = BN * KCPR / NT, VCH = BN * VCPR / NT;
   static_assert(KCH >= 1 && VCH >= 1, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * VP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * DV];  // swizzled for transposed reads
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -75,7 +74,7 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o1[i] = o2[i] = f32x16{};
   RowState st1, st2;
-  const VtLane vl(lane);
+  const TrLane<DV> vl(lane);
 
   i32x4 kr[KCH], vr[VCH];
   auto gload = [&](int nt) {
@@ -99,7 +98,7 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = tid + NT * c, row = idx / VCPR, col = idx % VCPR;
-      *(i32x4*)&Vs[buf][row * VP + col * 8] = vr[c];
+      *(i32x4*)&Vs[buf][tr_tile_off<DV>(row, col * 8)] = vr[c];
     }
   };
 
@@ -138,7 +137,7 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int t = 0; t < NPS; ++t) {
-        const bf16x8 vf = vt_operand<VP>(Vs[buf], t, db * 32, vl);
+        const bf16x8 vf = vt_operand<DV>(Vs[buf], t, db * 32, vl);
         o1[db] = mfma32(vf, pb1[t], o1[db]);
         o2[db] = mfma32(vf, pb2[t], o2[db]);
       }

@@ -31,11 +31,10 @@ constexpr int GN = 128;  // output channels per workgroup
 constexpr int GK = 64;   // K chunk staged in LDS
 constexpr int NT = 256;
 constexpr int MP = GK + 8;   // m tile pitch: 8 rows -> 8 distinct 16-byte bank groups
-constexpr int WP = GN + 16;  // W tile pitch: 4 rows -> 4 distinct 32-byte bank groups
 
 __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ms[2][GM * MP];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][GK * WP];
+  __shared__ __attribute__((aligned(16))) bf16 Ws[2][GK * GN];  // swizzled for transposed reads
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -72,14 +71,16 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
     for (int c = 0; c < 4; ++c) {
       const int idx = tid + NT * c;
       *(i32x4*)&Ms[buf][(idx >> 3) * MP + (idx & 7) * 8] = mr[c];
-      *(i32x4*)&Ws[buf][(idx >> 4) * WP + (idx & 15) * 8] = wr[c];
+      *(i32x4*)&Ws[buf][tr_tile_off<GN>(idx >> 4, (idx & 15) * 8)] = wr[c];
     }
   };
 
   // W^T operand by transposed reads: lane (channel n, half hh) needs W[k0 + 8*hh + 0..7][n];
   // lane r of each 16-lane group points at row k0 + 8*hh + r/4 (+4), columns 16*g + 4*(r%4).
+  // Those rows are congruent to r/4 mod 4, so the tile swizzle is a per-lane constant.
   const int wr_row = 8 * hh + ((lane & 15) >> 2);
   const int wr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wr_xo = tr_swz<GN>((lane & 15) >> 2) << 5;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -97,9 +98,9 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
       bf16x8 wa[2], mb[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const bf16* wp = &Ws[buf][(ks * 16 + wr_row) * WP + wn * 64 + nb * 32 + wr_col];
+        const bf16* wp = &Ws[buf][(ks * 16 + wr_row) * GN + ((wn * 64 + nb * 32 + wr_col) ^ wr_xo)];
         const i16x4 lo = lds_read_tr16(wp);
-        const i16x4 hi = lds_read_tr16(wp + 4 * WP);
+        const i16x4 hi = lds_read_tr16(wp + 4 * GN);
         wa[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
