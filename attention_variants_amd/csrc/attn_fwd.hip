@@ -11,8 +11,11 @@
 // is one whole tile and the multi-dimensional tile grid is linearised into one
 // physical grid dimension).  The mapping onto CDNA4 is this file's own:
 //
-//  * One workgroup = 4 waves = 128 query rows of one (batch, query head);
-//    each wave owns 32 rows for the whole KV loop.
+//  * One workgroup = 4 waves of one (batch, query head); each wave owns
+//    32*QB query rows for the whole KV loop (QB = 2 blocks of 32 at D <= 64,
+//    1 at D = 128).  Every K fragment and every transposed V fragment read
+//    from LDS feeds the MFMAs of all QB blocks, which halves LDS traffic per
+//    FLOP and gives each wave two independent softmax/MFMA chains.
 //  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //    MFMA.  In its output layout every lane holds 16 keys of ONE query
 //    (lanes l and l^32 share the query), so the row max is an in-register
@@ -50,33 +53,27 @@
 namespace av {
 namespace {
 
-constexpr int BM = kAttnBM;  // query rows per workgroup
-constexpr int BN = 64;       // keys per KV tile
-constexpr int NT = 256;      // threads per workgroup
+constexpr int BN = 64;   // keys per KV tile
+constexpr int NT = 256;  // threads per workgroup (4 waves)
 
-// Waves per SIMD each instantiation's register budget is sized for.  Four
-// (<= 128 VGPRs; the LDS of four 38 KB workgroups also fits a CU) where the
-// code fits without spilling, else three (<= 168 VGPRs); two at D = 128.
+// Waves per SIMD each instantiation's register budget is sized for.
 template <int D, int SM, int MK>
 constexpr int min_waves() {
-  if (D <= 32) return 4;
-  if (D == 64)
-    return ((SM == SM_NONE && (MK == MK_NONE || MK == MK_CAUSAL || MK == MK_WINDOW)) ||
-            (SM == SM_SOFTCAP_FIXED && MK == MK_NONE))
-               ? 4
-               : 3;
   return 2;
 }
 
 template <int D, int SM, int MK>
 __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int QB = attn_qb(D);     // 32-row query blocks per wave
+  constexpr int BM = attn_bm(D);     // query rows per workgroup
+  constexpr int WQ = 32 * QB;        // query rows per wave
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
   constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
   constexpr int NDS = D / 16;        // k-steps of the QK^T MFMA
   constexpr int NPS = BN / 16;       // k-steps of the PV MFMA
   constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
   constexpr int NCH = BN * CPR / NT; // chunks per thread per tensor
-  constexpr int KP = D + 8;          // K row pitch (elements): 8 rows hit 8 distinct 16-byte bank groups
+  constexpr int KP = D + 8;          // K row pitch (elements): 16 rows hit 16 distinct 16-byte bank slots
   static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
@@ -97,11 +94,13 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   const int hk = hq / a.g;
   const int mt = (MK == MK_CAUSAL || MK == MK_PREFIX) ? (a.nM - 1 - mt_lin) : mt_lin;
   const int q0 = mt * BM;
-  const int qw = q0 + 32 * __builtin_amdgcn_readfirstlane(w);  // first query row of this wave
-  const int qi = qw + l32;                                       // this lane's query row
+  const int qw = q0 + WQ * __builtin_amdgcn_readfirstlane(w);  // first query row of this wave
+  int qi[QB];                                                  // this lane's query row per block
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qi[qb] = qw + 32 * qb + l32;
   const int qlast = min(q0 + BM, a.Sq) - 1;
   const bool wave_live = qw < a.Sq;
-  const int qwlast = min(qw + 31, a.Sq - 1);
+  const int qwlast = min(qw + WQ - 1, a.Sq - 1);
 
   const size_t qoff = ((size_t)b * a.Hq + hq) * (size_t)a.Sq * D;
   const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
@@ -113,7 +112,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   // ---- analytic KV tile range [n_lo, n_hi) of the workgroup
   const int nKV = (a.Skv + BN - 1) / BN;
   int n_lo = 0, n_hi = nKV;
-  int dq = 0, dqw = 0, dqwlast = 0;
+  int dq[QB] = {};
+  int dqw = 0, dqwlast = 0;
   if constexpr (MK == MK_CAUSAL) {
     n_hi = min(nKV, qlast / BN + 1);
   } else if constexpr (MK == MK_WINDOW) {
@@ -127,29 +127,30 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     const int kend = wave_upper_bound(docrow, a.Skv, dlast);
     n_lo = kstart / BN;
     n_hi = min(nKV, (kend + BN - 1) / BN);
-    dq = docrow[min(qi, a.Sq - 1)];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) dq[qb] = docrow[min(qi[qb], a.Sq - 1)];
     dqw = __builtin_amdgcn_readfirstlane(docrow[min(qw, a.Sq - 1)]);
     dqwlast = __builtin_amdgcn_readfirstlane(docrow[max(qwlast, 0)]);
   }
 
-  // ---- Q^T operands in registers: lane holds query qi, 8 consecutive d per k-step
-  bf16x8 qreg[NDS];
+  // ---- Q^T operands in registers: lane holds query qi[qb], 8 consecutive d per k-step
+  bf16x8 qreg[QB][NDS];
 #pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    const uint32_t off = (uint32_t)(qi * D + s * 16 + hh * 8) * 2;
-    qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off));
-  }
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      qreg[qb][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(qi[qb] * D + s * 16 + hh * 8) * 2));
 
-  f32x16 o[NDB];
+  f32x16 o[QB][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-  RowState st;
-  if constexpr (SM == SM_SOFTCAP_FIXED) st.m_ref = a.softcap * kLog2e;  // the scores hold t - m_ref already
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[qb][db] = f32x16{};
+  RowState st[QB];
   const TrLane<D> vl(lane);
 
-  // score-modifier constants
   // ALiBi, log2 units: bias(kb, j) = slope * (kj - qi) with kj = n0 + 4*hh + 32*kb + 8*(j/4) + j%4
-  //   = [slope * (n0 + 4*hh - qi + j%4)]  (4 per-lane values per tile)
+  //   = [slope * (n0 + 4*hh - qi + j%4)]  (4 per-lane values per tile and block)
   //   + [slope * (32*kb + 8*(j/4))]       (wave-uniform, one SGPR each)
   float alibi_slope2 = 0.f;
   float alibi_u[NKB * 4];
@@ -158,19 +159,22 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < NKB * 4; ++g) alibi_u[g] = uniform_f(alibi_slope2 * (float)(8 * g));
   }
-  // Evoformer pair bias of head hq, rows qi: 4 keys (8 bytes) per load
+  // Evoformer pair bias of head hq: 4 keys (8 bytes) per load
   const auto brs = make_rsrc(SM == SM_BIAS ? (const bf16*)a.bias + (size_t)hq * a.Sq * a.Skv : nullptr,
                              SM == SM_BIAS ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
-  const float cap2 = a.softcap * kLog2e;  // softcap in log2 units
+  // softcap in log2 units: cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k)),
+  // from exp2 and rcp; with the fixed reference the kernel keeps t - cap2 (one op less)
+  const float cap2 = a.softcap * kLog2e;
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
-  // cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k)), from exp2 and rcp;
-  // with the fixed reference the kernel keeps t - cap2 (one op less)
   const float cap_off = SM == SM_SOFTCAP_FIXED ? 0.f : cap2;
   auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap_off); };
+  if constexpr (SM == SM_SOFTCAP_FIXED) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = cap2;  // the scores hold t - m_ref already
+  }
 
   i32x4 kr[NCH], vr[NCH];
   int dr = 0;
-
   auto gload = [&](int nt) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -206,62 +210,76 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   auto tile = [&](bool full, int buf, int n0) {
     const int kbase = n0 + 4 * hh;
     // ---- pair bias loads issued ahead of the MFMAs: keys kbase + 32*kb + 8*g + 0..3
-    i32x4 braw[NKB * 2];
+    i32x4 braw[QB][NKB * 2];
     if constexpr (SM == SM_BIAS) {
-      const uint32_t rowoff = (uint32_t)(qi * a.Skv + kbase) * 2;
-      if (a.Skv % 4 == 0) {
 #pragma unroll
-        for (int g = 0; g < NKB * 4; g += 2) {
-          const auto lo = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16, 0, 0);
-          const auto hi = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16 + 16, 0, 0);
-          braw[g >> 1] = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
-        }
-      } else {  // rows not 8-byte aligned: 16-bit loads
+      for (int qb = 0; qb < QB; ++qb) {
+        const uint32_t rowoff = (uint32_t)(qi[qb] * a.Skv + kbase) * 2;
+        if (a.Skv % 4 == 0) {
 #pragma unroll
-        for (int g = 0; g < NKB * 4; ++g) {
-          int w2[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const uint32_t o0 = rowoff + g * 16 + h2 * 4;
-            const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0, 0, 0);
-            const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0 + 2, 0, 0);
-            w2[h2] = (int)(x0 | (x1 << 16));
+          for (int g = 0; g < NKB * 4; g += 2) {
+            const auto lo = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16, 0, 0);
+            const auto hi = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16 + 16, 0, 0);
+            braw[qb][g >> 1] = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
           }
-          braw[g >> 1][(g & 1) * 2] = w2[0];
-          braw[g >> 1][(g & 1) * 2 + 1] = w2[1];
+        } else {  // rows not 8-byte aligned: 16-bit loads
+#pragma unroll
+          for (int g = 0; g < NKB * 4; ++g) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const uint32_t o0 = rowoff + g * 16 + h2 * 4;
+              const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0, 0, 0);
+              const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0 + 2, 0, 0);
+              braw[qb][g >> 1][(g & 1) * 2 + h2] = (int)(x0 | (x1 << 16));
+            }
+          }
         }
       }
     }
-    // Exponent reference: a softcap with a small cap has bounded scores, so
-    // its reference sits at the cap and no max is taken; every other variant
-    // tracks the tile max with the lazy rescale.
-    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
-    bf16x8 pb[NPS];
-    {
-      // ---- S^T = K Q^T : s[kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = qk_block<NDS, KP>(Ks[buf], kb, 0, qreg, l32, hh);
 
+    // ---- S^T = K Q^T : s[qb][kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi[qb];
+    //      each K fragment read from LDS feeds the MFMAs of every query block
+    f32x16 s[QB][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+      const bf16* krow = Ks[buf] + (kb * 32 + l32) * KP + hh * 8;
+#pragma unroll
+      for (int st_ = 0; st_ < NDS; ++st_) {
+        const bf16x8 kf = *(const bf16x8*)(krow + st_ * 16);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(kf, qreg[qb][st_], s[qb][kb]);
+      }
+    }
+
+    // ---- per query block: score modifier, mask, reference, exp, PV.  Block
+    //      qb's VALU work overlaps the MFMAs still in flight for the other
+    //      block (QK^T of block 1 while block 0 is exponentiated, PV of block 0
+    //      while block 1 is); the V fragments are read once and reused.
+    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
+    bf16x8 vf[NDB][NPS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
       if constexpr (SM != SM_NONE) {
         float ab[4];
         if constexpr (SM == SM_ALIBI) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi + c);
+          for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi[qb] + c);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             if constexpr (SM == SM_ALIBI) {
-              s[kb][j] = fmaf(s[kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
+              s[qb][kb][j] = fmaf(s[qb][kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
             } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
-              s[kb][j] = softcap_t(s[kb][j]);
+              s[qb][kb][j] = softcap_t(s[qb][kb][j]);
             } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
-              const int wd = braw[(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
+              const int wd = braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
               const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
-              s[kb][j] = fmaf(s[kb][j], a.c, bv * kLog2e);
+              s[qb][kb][j] = fmaf(s[qb][kb][j], a.c, bv * kLog2e);
             }
           }
       }
@@ -274,31 +292,38 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
             const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
             bool ok = off < a.Skv - kbase;
             if constexpr (MK == MK_CAUSAL) {
-              ok = ok && (off <= qi - kbase);
+              ok = ok && (off <= qi[qb] - kbase);
             } else if constexpr (MK == MK_WINDOW) {
-              const int rel = qi - kbase;
+              const int rel = qi[qb] - kbase;
               ok = ok && (off <= rel) && (off > rel - a.window);
             } else if constexpr (MK == MK_PREFIX) {
-              ok = ok && ((off < a.prefix - kbase) || (off <= qi - kbase));
+              ok = ok && ((off < a.prefix - kbase) || (off <= qi[qb] - kbase));
             } else if constexpr (MK == MK_DOC) {
-              ok = ok && (Ds[buf][off + 4 * hh] == dq);
+              ok = ok && (Ds[buf][off + 4 * hh] == dq[qb]);
             }
-            s[kb][j] = ok ? s[kb][j] : neg_inf();
+            s[qb][kb][j] = ok ? s[qb][kb][j] : neg_inf();
           }
         }
       }
+      // ---- exponent reference: a softcap with a small cap has bounded scores,
+      //      so its reference sits at the cap and no max is taken; every other
+      //      variant tracks the tile max with the lazy rescale
       if constexpr (SM != SM_SOFTCAP_FIXED) {
-        const float lmax = xhalf_max(block_max<NKB>(s));
-        st.update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o);
+        const float lmax = xhalf_max(block_max<NKB>(s[qb]));
+        st[qb].template update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o[qb]);
       }
-      st.l += exp_pack_sum<NKB, MODE>(s, a.c, st.m_sub, pb);
+      // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
+      bf16x8 pb[NPS];
+      st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb);
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int t = 0; t < NPS; ++t) {
+          if (qb == 0) vf[db][t] = vt_operand<D>(Vs[buf], t, db * 32, vl);
+          o[qb][db] = mfma32(vf[db][t], pb[t], o[qb][db]);
+        }
     }
-
-    // ---- O^T += V^T P^T, V^T operand via two transposed LDS reads per MFMA
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int t = 0; t < NPS; ++t) o[db] = mfma32(vt_operand<D>(Vs[buf], t, db * 32, vl), pb[t], o[db]);
   };
 
   if (n_lo < n_hi) gload(n_lo);
@@ -332,41 +357,47 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   }
 
   // ---- epilogue: O / l, bf16 store, optional LSE
-  const float l_tot = xhalf_sum(st.l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qi < a.Sq && SM == SM_BIAS) {
-    // Evoformer: out[b, qi, hq*D + d] = sigmoid(gate[b, hq, qi, d]) * O[d] / l
-    bf16* orow = (bf16*)a.o + ((size_t)b * a.Sq + qi) * (size_t)(a.Hq * D) + (size_t)hq * D;
-    const bf16* grow = (const bf16*)a.gate + qoff + (size_t)qi * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = xhalf_sum(st[qb].l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const int q = qi[qb];
+    if (q >= a.Sq) continue;
+    if constexpr (SM == SM_BIAS) {
+      // Evoformer: out[b, q, hq*D + d] = sigmoid(gate[b, hq, q, d]) * O[d] / l
+      bf16* orow = (bf16*)a.o + ((size_t)b * a.Sq + q) * (size_t)(a.Hq * D) + (size_t)hq * D;
+      const bf16* grow = (const bf16*)a.gate + qoff + (size_t)q * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * hh;
-        const bf16x4 gv = *(const bf16x4*)(grow + d0);
-        bf16x4 val;
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sig = rcp_fast(1.f + exp2_fast(-(float)gv[e] * kLog2e));
-          val[e] = (bf16)(o[db][g4 * 4 + e] * inv * sig);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = db * 32 + 8 * g4 + 4 * hh;
+          const bf16x4 gv = *(const bf16x4*)(grow + d0);
+          bf16x4 val;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sig = rcp_fast(1.f + exp2_fast(-(float)gv[e] * kLog2e));
+            val[e] = (bf16)(o[qb][db][g4 * 4 + e] * inv * sig);
+          }
+          *(bf16x4*)(orow + d0) = val;
         }
-        *(bf16x4*)(orow + d0) = val;
       }
-    }
-  } else if (qi < a.Sq) {
-    bf16* orow = (bf16*)a.o + qoff + (size_t)qi * D;
+    } else {
+      bf16* orow = (bf16*)a.o + qoff + (size_t)q * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 val;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (bf16)(o[db][g4 * 4 + e] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = val;
+          for (int e = 0; e < 4; ++e) val[e] = (bf16)(o[qb][db][g4 * 4 + e] * inv);
+          *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = val;
+        }
       }
-    }
-    if (a.lse != nullptr && hh == 0) {
-      a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi] = l_tot > 0.f ? (st.m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
+      if (a.lse != nullptr && hh == 0) {
+        a.lse[((size_t)b * a.Hq + hq) * a.Sq + q] =
+            l_tot > 0.f ? (st[qb].m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
+      }
     }
   }
 }

@@ -122,10 +122,11 @@ struct RowState {
 
 // p = exp2(s * c - m_sub) (MODE 0), exp2(s - m_sub) (MODE 1) or exp2(s)
 // (MODE 2) for the registers of NB S^T blocks, packed to bf16 P^T operands
-// pb[2*NB]; returns this lane's sum of the bf16 values.
+// pb[2*NB]; returns this lane's sum of the bf16 values.  The sum runs in four
+// independent partial accumulators so the dot2 chain does not serialise.
 template <int NB, int MODE>
 __device__ __forceinline__ float exp_pack_sum(const f32x16* s, float c, float m_sub, bf16x8* pb) {
-  float acc = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb) {
 #pragma unroll
@@ -139,30 +140,12 @@ __device__ __forceinline__ float exp_pack_sum(const f32x16* s, float c, float m_
         x1 -= m_sub;
       }
       const bf16x2 pp = {(bf16)exp2_fast(x0), (bf16)exp2_fast(x1)};
-      acc = add_bf16_pair(pp, acc);
+      acc[(j >> 1) & 3] = add_bf16_pair(pp, acc[(j >> 1) & 3]);
       pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
       pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
     }
   }
-  return acc;
-}
-
-// p = exp2(s * c - m_sub) for the registers of NB S^T blocks, packed to bf16
-// P^T operands pb[2*NB]; adds the bf16 values to the lane's row sum.
-template <int NB>
-__device__ __forceinline__ void exp_pack(const f32x16* s, float c, RowState& st, bf16x8* pb) {
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb) {
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = exp2_fast(fmaf(s[kb][j], c, -st.m_sub));
-      const float p1 = exp2_fast(fmaf(s[kb][j + 1], c, -st.m_sub));
-      const bf16x2 pp = {(bf16)p0, (bf16)p1};
-      st.l = add_bf16_pair(pp, st.l);
-      pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
-      pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
-    }
-  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 }  // namespace av

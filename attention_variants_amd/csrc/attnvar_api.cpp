@@ -64,9 +64,9 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
   // Per-slice byte offsets are 32-bit inside the kernel; query rows of a
   // ragged last tile may index up to BM-1 rows past Sq.
-  if ((uint64_t)(Sq + av::kAttnBM) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  if ((uint64_t)(Sq + av::kAttnBMMax) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
   if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
-  const int64_t nM = ((int64_t)Sq + av::kAttnBM - 1) / av::kAttnBM;
+  const int64_t nM = ((int64_t)Sq + av::attn_bm(D) - 1) / av::attn_bm(D);
   const int64_t total = (int64_t)B * Hq * nM;
   if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
   if (total == 0) return AV_OK;

@@ -37,8 +37,14 @@ struct AttnArgs {
   int fixed_ref;     // softcap with 2 * cap * log2(e) <= 96: exponent reference fixed at the cap
 };
 
-// Query rows per workgroup of the attention forward kernel.
+// Query rows per workgroup: the differential kernel uses 4 waves x 32 rows;
+// the fused attention kernel uses 4 waves x 32*QB rows, QB = query blocks per
+// wave (2 at D <= 64, so every K/V fragment read from LDS feeds two MFMAs;
+// 1 at D = 128, where two blocks do not fit the register file).
 constexpr int kAttnBM = 128;
+constexpr int attn_qb(int D) { return D <= 64 ? 2 : 1; }
+constexpr int attn_bm(int D) { return 4 * 32 * attn_qb(D); }
+constexpr int kAttnBMMax = 256;
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
 // Evoformer gated attention over the projected workspace (D = 32, SM_BIAS).

@@ -131,8 +131,8 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
     st1.update<NDB>(xhalf_max(block_max<1>(&s1)) * a.c, o1);
     st2.update<NDB>(xhalf_max(block_max<1>(&s2)) * a.c, o2);
     bf16x8 pb1[NPS], pb2[NPS];
-    exp_pack<1>(&s1, a.c, st1, pb1);
-    exp_pack<1>(&s2, a.c, st2, pb2);
+    st1.l += exp_pack_sum<1, 0>(&s1, a.c, st1.m_sub, pb1);
+    st2.l += exp_pack_sum<1, 0>(&s2, a.c, st2.m_sub, pb2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
