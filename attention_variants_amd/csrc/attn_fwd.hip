@@ -56,16 +56,17 @@ namespace {
 constexpr int BN = 64;   // keys per KV tile
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 
-// Waves per SIMD each instantiation's register budget is sized for.
+// Waves per SIMD each instantiation's register budget is sized for: two
+// with two query blocks per wave or D = 128, three with one block.
 template <int D, int SM, int MK>
 constexpr int min_waves() {
-  return 2;
+  return attn_qb(D, MK) == 2 || D == 128 ? 2 : 3;
 }
 
 template <int D, int SM, int MK>
 __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int QB = attn_qb(D);     // 32-row query blocks per wave
-  constexpr int BM = attn_bm(D);     // query rows per workgroup
+  constexpr int QB = attn_qb(D, MK);  // 32-row query blocks per wave
+  constexpr int BM = attn_bm(D, MK);  // query rows per workgroup
   constexpr int WQ = 32 * QB;        // query rows per wave
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
   constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
@@ -253,12 +254,6 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
     }
 
-    // ---- per query block: score modifier, mask, reference, exp, PV.  Block
-    //      qb's VALU work overlaps the MFMAs still in flight for the other
-    //      block (QK^T of block 1 while block 0 is exponentiated, PV of block 0
-    //      while block 1 is); the V fragments are read once and reused.
-    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
-    bf16x8 vf[NDB][NPS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
@@ -305,25 +300,42 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
           }
         }
       }
-      // ---- exponent reference: a softcap with a small cap has bounded scores,
-      //      so its reference sits at the cap and no max is taken; every other
-      //      variant tracks the tile max with the lazy rescale
-      if constexpr (SM != SM_SOFTCAP_FIXED) {
-        const float lmax = xhalf_max(block_max<NKB>(s[qb]));
-        st[qb].template update<NDB>(SM == SM_NONE ? lmax * a.c : lmax, o[qb]);
-      }
-      // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
-      bf16x8 pb[NPS];
-      st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb);
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int t = 0; t < NPS; ++t) {
-          if (qb == 0) vf[db][t] = vt_operand<D>(Vs[buf], t, db * 32, vl);
-          o[qb][db] = mfma32(vf[db][t], pb[t], o[qb][db]);
-        }
     }
+
+    // ---- exponent reference: a softcap with a small cap has bounded scores,
+    //      so its reference sits at the cap and no max is taken; every other
+    //      variant tracks the tile max with the lazy rescale (one wave-uniform
+    //      decision for all query blocks)
+    if constexpr (SM != SM_SOFTCAP_FIXED) {
+      float tmax[QB];
+      bool grow = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float lmax = xhalf_max(block_max<NKB>(s[qb]));
+        tmax[qb] = SM == SM_NONE ? lmax * a.c : lmax;
+        grow |= tmax[qb] > st[qb].m_ref + kLazyTau;
+      }
+      if (any_lane(grow)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) st[qb].template raise<NDB>(tmax[qb], o[qb]);
+      }
+    }
+
+    // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
+    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
+    bf16x8 pb[QB][NPS];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+
+    // ---- O^T += V^T P^T; each transposed V fragment feeds every query block
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < NPS; ++t) {
+        const bf16x8 vf = vt_operand<D>(Vs[buf], t, db * 32, vl);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf, pb[qb][t], o[qb][db]);
+      }
   };
 
   if (n_lo < n_hi) gload(n_lo);

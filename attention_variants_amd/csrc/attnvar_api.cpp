@@ -66,7 +66,8 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   // ragged last tile may index up to BM-1 rows past Sq.
   if ((uint64_t)(Sq + av::kAttnBMMax) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
   if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
-  const int64_t nM = ((int64_t)Sq + av::attn_bm(D) - 1) / av::attn_bm(D);
+  const int bm = av::attn_bm(D, var->mask);
+  const int64_t nM = ((int64_t)Sq + bm - 1) / bm;
   const int64_t total = (int64_t)B * Hq * nM;
   if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
   if (total == 0) return AV_OK;

@@ -161,7 +161,7 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   t.Hq = t.Hkv = a.H;
   t.Sq = t.Skv = a.Nr;
   t.g = 1;
-  t.nM = (a.Nr + attn_bm(32) - 1) / attn_bm(32);
+  t.nM = (a.Nr + attn_bm(32, MK_NONE) - 1) / attn_bm(32, MK_NONE);
   t.total = a.Ns * a.H * t.nM;
   t.c = a.c;
   t.scale = a.c / 1.4426950408889634f;

@@ -105,13 +105,22 @@ def _dev(bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def time_launches(fns, steps, warmup):
-    """Run each callable of `fns` once per step; return (total_ms, [per-fn mean ms])."""
+def time_launches(fns, steps, warmup, min_warm_s=0.2):
+    """Run each callable of `fns` once per step; return (total_ms, [per-fn mean ms]).
+
+    Warm-up runs at least `warmup` rounds and at least `min_warm_s` seconds, so
+    the GPU clock has ramped up after any idle gap (input generation on the
+    host) before timing starts."""
     import torch
 
-    for _ in range(warmup):
+    t_end = time.perf_counter() + min_warm_s
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         for f in fns:
             f()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     starts = [[torch.cuda.Event(enable_timing=True) for _ in range(steps)] for _ in fns]
     ends = [[torch.cuda.Event(enable_timing=True) for _ in range(steps)] for _ in fns]
