@@ -333,6 +333,29 @@ def run_profile(what, steps):
     import attention_variants_amd as av
 
     av.load_library()
+    if what == "evoformer":
+        Ns, Nr, Cm, Hh, dh = 128, 256, 256, 8, 32
+        x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
+        t = {n: _dev(x[n], dev) for n in x}
+        ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
+        out = torch.empty((Ns, Nr, Hh * dh), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=Hh, dh=dh,
+                                        workspace=ws, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "evoformer", "Ns": Ns, "Nr": Nr, "launches": steps}))
+        return
+    if what == "diff":
+        x = wi.diff_inputs(4, 16, 4096)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(v)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.diff_attn_fwd(q, k, v, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "diff", "B": 4, "H": 16, "S": 4096, "launches": steps}))
+        return
     B, H, S, D = 4, 16, 4096, 64
     x = wi.attention_inputs(B, H, H, S, S, D)
     q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -353,7 +376,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
-    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy"], default=None,
+    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "diff"], default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
