@@ -82,7 +82,7 @@ def kernel_source_sha():
 def measured_traffic():
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "attn_fwd_vanilla_S4096_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", "attn_fwd_S4096_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -202,7 +202,7 @@ def run_headline(args):
         variants[sm] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     dom = max(range(3), key=lambda i: per_ms[i])
     achieved = fl / (per_ms[dom] * 1e-3) / 1e12
-    traffic = measured_traffic() if mods[dom] == "none" else None
+    traffic = measured_traffic()
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
