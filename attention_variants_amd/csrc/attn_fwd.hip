@@ -278,54 +278,83 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
             }
           }
       }
-      // ---- element mask, partial tiles only (wave-uniform branch)
+      // ---- element mask, partial tiles only (wave-uniform branch).  The
+      //      limits pass through an empty asm so that the compares are not
+      //      hoisted out of the branch into every tile.
       if (!full) {
+        int lim = a.Skv - kbase, rel = qi[qb] - kbase, pre = a.prefix - kbase, wlo = rel - a.window;
+        asm volatile("" : "+v"(lim), "+v"(rel), "+v"(pre), "+v"(wlo));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-            bool ok = off < a.Skv - kbase;
+            bool ok = off < lim;
             if constexpr (MK == MK_CAUSAL) {
-              ok = ok && (off <= qi[qb] - kbase);
+              ok = ok && (off <= rel);
             } else if constexpr (MK == MK_WINDOW) {
-              const int rel = qi[qb] - kbase;
-              ok = ok && (off <= rel) && (off > rel - a.window);
+              ok = ok && (off <= rel) && (off > wlo);
             } else if constexpr (MK == MK_PREFIX) {
-              ok = ok && ((off < a.prefix - kbase) || (off <= qi[qb] - kbase));
+              ok = ok && ((off < pre) || (off <= rel));
             } else if constexpr (MK == MK_DOC) {
               ok = ok && (Ds[buf][off + 4 * hh] == dq[qb]);
             }
             s[qb][kb][j] = ok ? s[qb][kb][j] : neg_inf();
+            if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bounds the live compare masks
           }
         }
       }
     }
 
-    // ---- exponent reference: a softcap with a small cap has bounded scores,
-    //      so its reference sits at the cap and no max is taken; every other
-    //      variant tracks the tile max with the lazy rescale (one wave-uniform
-    //      decision for all query blocks)
-    if constexpr (SM != SM_SOFTCAP_FIXED) {
-      float tmax[QB];
-      bool grow = false;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float lmax = xhalf_max(block_max<NKB>(s[qb]));
-        tmax[qb] = SM == SM_NONE ? lmax * a.c : lmax;
-        grow |= tmax[qb] > st[qb].m_ref + kLazyTau;
-      }
-      if (any_lane(grow)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) st[qb].template raise<NDB>(tmax[qb], o[qb]);
-      }
-    }
-
-    // ---- p = exp2(t - m_ref) -> bf16 P^T operands; row sum of the bf16 values
+    // ---- exponent reference and p = exp2(t - m_ref) -> bf16 P^T operands,
+    //      with the row sum of the bf16 values
     constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
     bf16x8 pb[QB][NPS];
+    if constexpr (SM == SM_NONE || SM == SM_BIAS) {
+      // Optimistic: exponentiate against the current reference and keep the
+      // result unless some exponential exceeds 2^64 (then the tile sum does)
+      // or the row has no reference yet.  The reference is only ever a
+      // previous tile max, so the row's largest exponential stays >= 1; the
+      // max is taken only on the rare tiles that fail the check.
+      float tsum[QB];
+      bool redo = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+      for (int qb = 0; qb < QB; ++qb) {
+        tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+        redo |= (tsum[qb] > kOptBound) || (st[qb].m_ref == neg_inf());
+      }
+      if (any_lane(redo)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float rmax = xhalf_max(block_max<NKB>(s[qb]));
+          st[qb].template raise<NDB>(SM == SM_NONE ? rmax * a.c : rmax, o[qb]);
+          tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) st[qb].l += tsum[qb];
+    } else {
+      // ALiBi scores can climb along the row, so the tile max is tracked
+      // with the lazy rescale (one wave-uniform decision for all blocks; each
+      // lane tests its own half of the row, the raise uses the whole row).
+      // A softcap with a small cap has bounded scores: its reference sits at
+      // the cap and no max is taken.
+      if constexpr (SM != SM_SOFTCAP_FIXED) {
+        float hmax[QB];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          hmax[qb] = block_max<NKB>(s[qb]);
+          grow |= hmax[qb] > st[qb].thr;
+        }
+        if (any_lane(grow)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) st[qb].template raise<NDB>(xhalf_max(hmax[qb]), o[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+    }
 
     // ---- O^T += V^T P^T; each transposed V fragment feeds every query block
 #pragma unroll

@@ -19,6 +19,10 @@
 namespace av {
 
 constexpr float kLazyTau = 8.f;
+// Largest tile sum of exponentials accepted without taking the tile max
+// (2^64: exponentials, their bf16 copies and the fp32 accumulators stay far
+// from overflow).
+constexpr float kOptBound = 18446744073709551616.f;
 
 // S^T for key block kb of an LDS K tile (row pitch KP elements), over NSTEP
 // k-steps of 16 starting at column c0.
@@ -81,14 +85,20 @@ __device__ __forceinline__ void mask_block(f32x16& s, Keep keep) {
   }
 }
 
-// Max over the registers of NB S^T blocks (four independent chains).
+// Max over the registers of NB S^T blocks: four independent chains, each
+// step folding two new values (one v_max3).
 template <int NB>
 __device__ __forceinline__ float block_max(const f32x16* s) {
-  float mx[4] = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+  float mx[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) mx[c] = fmaxf(s[0][2 * c], s[0][2 * c + 1]);
 #pragma unroll
   for (int kb = 0; kb < NB; ++kb)
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) mx[(j >> 1) & 3] = fmaxf(mx[(j >> 1) & 3], fmaxf(s[kb][j], s[kb][j + 1]));
+    for (int j = (kb == 0 ? 8 : 0); j < 16; j += 2) {
+      const int c = (j >> 1) & 3;
+      mx[c] = fmaxf(fmaxf(mx[c], s[kb][j]), s[kb][j + 1]);
+    }
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
@@ -98,6 +108,7 @@ __device__ __forceinline__ float block_max(const f32x16* s) {
 struct RowState {
   float m_ref = neg_inf();  // exponent reference (log2 units), equal in lanes l and l^32
   float m_sub = 0.f;        // m_ref with -inf replaced by 0
+  float thr = neg_inf();    // m_ref + kLazyTau: a tile max above it raises the reference
   float l = 0.f;            // this lane's share of the row sum, relative to m_ref
 
   // Raise the reference to the tile max where it is higher; rescale l and the
@@ -112,11 +123,12 @@ struct RowState {
     for (int i = 0; i < NO; ++i) o[i] *= alpha;
     m_ref = m_new;
     m_sub = m_new_sub;
+    thr = m_new + kLazyTau;
   }
   // Lazy variant: only when some lane's tile max exceeds m_ref by > 2^kLazyTau.
   template <int NO>
   __device__ __forceinline__ void update(float tile_max, f32x16* o) {
-    if (any_lane(tile_max > m_ref + kLazyTau)) raise<NO>(tile_max, o);
+    if (any_lane(tile_max > thr)) raise<NO>(tile_max, o);
   }
 };
 
