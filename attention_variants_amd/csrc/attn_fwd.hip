@@ -150,6 +150,23 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   RowState st[QB];
   const TrLane<D> vl(lane);
 
+  // Evoformer gate pre-activations of this lane's output channels, loaded
+  // up front so that their latency hides behind the KV loop
+  bf16x4 gate[QB][SM == SM_BIAS ? NDB * 4 : 1];
+  if constexpr (SM == SM_BIAS) {
+    const auto grs = make_rsrc((const bf16*)a.gate + qoff, (uint32_t)a.Sq * D * 2);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const auto w2 = __builtin_amdgcn_raw_buffer_load_b64(
+              grs, (uint32_t)(qi[qb] * D + db * 32 + 8 * g4 + 4 * hh) * 2, 0, 0);
+          gate[qb][db * 4 + g4] = __builtin_bit_cast(bf16x4, w2);
+        }
+  }
+
   // ALiBi, log2 units: bias(kb, j) = slope * (kj - qi) with kj = n0 + 4*hh + 32*kb + 8*(j/4) + j%4
   //   = [slope * (n0 + 4*hh - qi + j%4)]  (4 per-lane values per tile and block)
   //   + [slope * (32*kb + 8*(j/4))]       (wave-uniform, one SGPR each)
@@ -163,12 +180,16 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   // Evoformer pair bias of head hq: 4 keys (8 bytes) per load
   const auto brs = make_rsrc(SM == SM_BIAS ? (const bf16*)a.bias + (size_t)hq * a.Sq * a.Skv : nullptr,
                              SM == SM_BIAS ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
-  // softcap in log2 units: cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k)),
-  // from exp2 and rcp; with the fixed reference the kernel keeps t - cap2 (one op less)
+  // softcap in log2 units: cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k))
+  // = cap2 - 1 / fma(E, invK, invK) with E = 2^(raw*sc_k), invK = 1/(2*cap2): one exp2,
+  // one fma, one rcp; with the fixed reference the kernel keeps t - cap2
   const float cap2 = a.softcap * kLog2e;
   const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
-  const float cap_off = SM == SM_SOFTCAP_FIXED ? 0.f : cap2;
-  auto softcap_t = [&](float raw) { return fmaf(-2.f * cap2, rcp_fast(1.f + exp2_fast(raw * sc_k)), cap_off); };
+  const float invK = 0.5f / cap2;
+  auto softcap_t = [&](float raw) {
+    const float r = rcp_fast(fmaf(exp2_fast(raw * sc_k), invK, invK));
+    return SM == SM_SOFTCAP_FIXED ? -r : cap2 - r;
+  };
   if constexpr (SM == SM_SOFTCAP_FIXED) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = cap2;  // the scores hold t - m_ref already
@@ -205,38 +226,43 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
   };
 
+  // Evoformer pair bias of this lane's (query, key) elements: keys
+  // n0 + 4*hh + 32*kb + 8*g + 0..3, loaded one tile ahead of its use
+  i32x4 braw[QB][NKB * 2];
+  auto bias_load = [&](int n0) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint32_t rowoff = (uint32_t)(qi[qb] * a.Skv + n0 + 4 * hh) * 2;
+      if (a.Skv % 4 == 0) {
+#pragma unroll
+        for (int g = 0; g < NKB * 4; g += 2) {
+          const auto lo = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16, 0, 0);
+          const auto hi = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16 + 16, 0, 0);
+          braw[qb][g >> 1] = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
+        }
+      } else {  // rows not 8-byte aligned: 16-bit loads
+#pragma unroll
+        for (int g = 0; g < NKB * 4; ++g) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const uint32_t o0 = rowoff + g * 16 + h2 * 4;
+            const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0, 0, 0);
+            const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0 + 2, 0, 0);
+            braw[qb][g >> 1][(g & 1) * 2 + h2] = (int)(x0 | (x1 << 16));
+          }
+        }
+      }
+    }
+  };
+  // exponent argument scale: scores of vanilla attention are raw q.k, pair-bias
+  // scores are q.k*scale + bias (natural units); the other modifiers produce log2 units
+  const float cexp = SM == SM_BIAS ? kLog2e : a.c;
+
   // One KV tile for this wave.  Only the element mask depends on the tile
   // class, and it edits the score registers in place, so the MFMA
   // accumulators flow through a single path (no copies at a merge point).
   auto tile = [&](bool full, int buf, int n0) {
     const int kbase = n0 + 4 * hh;
-    // ---- pair bias loads issued ahead of the MFMAs: keys kbase + 32*kb + 8*g + 0..3
-    i32x4 braw[QB][NKB * 2];
-    if constexpr (SM == SM_BIAS) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const uint32_t rowoff = (uint32_t)(qi[qb] * a.Skv + kbase) * 2;
-        if (a.Skv % 4 == 0) {
-#pragma unroll
-          for (int g = 0; g < NKB * 4; g += 2) {
-            const auto lo = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16, 0, 0);
-            const auto hi = __builtin_amdgcn_raw_buffer_load_b64(brs, rowoff + g * 16 + 16, 0, 0);
-            braw[qb][g >> 1] = i32x4{(int)lo[0], (int)lo[1], (int)hi[0], (int)hi[1]};
-          }
-        } else {  // rows not 8-byte aligned: 16-bit loads
-#pragma unroll
-          for (int g = 0; g < NKB * 4; ++g) {
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const uint32_t o0 = rowoff + g * 16 + h2 * 4;
-              const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0, 0, 0);
-              const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, o0 + 2, 0, 0);
-              braw[qb][g >> 1][(g & 1) * 2 + h2] = (int)(x0 | (x1 << 16));
-            }
-          }
-        }
-      }
-    }
 
     // ---- S^T = K Q^T : s[qb][kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi[qb];
     //      each K fragment read from LDS feeds the MFMAs of every query block
@@ -256,12 +282,15 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // ---- score modifier (log2 units except vanilla, whose scale is folded into exp2)
+      // ---- score modifier: ALiBi and softcap in log2 units, pair bias in natural
+      //      units (q.k*scale + bias); vanilla keeps the raw q.k, its scale folded into exp2
       if constexpr (SM != SM_NONE) {
+        // ALiBi goes straight to the exponent argument, relative to the
+        // current reference: s*c + slope*(key - query) - m_sub
         float ab[4];
         if constexpr (SM == SM_ALIBI) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ab[c] = alibi_slope2 * (float)(kbase - qi[qb] + c);
+          for (int c = 0; c < 4; ++c) ab[c] = fmaf(alibi_slope2, (float)(kbase - qi[qb] + c), -st[qb].m_sub);
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -274,7 +303,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
             } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
               const int wd = braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
               const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
-              s[qb][kb][j] = fmaf(s[qb][kb][j], a.c, bv * kLog2e);
+              s[qb][kb][j] = fmaf(s[qb][kb][j], a.scale, bv);
             }
           }
       }
@@ -306,9 +335,13 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
     }
 
+    if constexpr (SM == SM_BIAS) {
+      if (n0 + BN < n_hi * BN) bias_load(n0 + BN);  // the next tile's bias, in flight during this one
+    }
+
     // ---- exponent reference and p = exp2(t - m_ref) -> bf16 P^T operands,
     //      with the row sum of the bf16 values
-    constexpr int MODE = SM == SM_NONE ? 0 : SM == SM_SOFTCAP_FIXED ? 2 : 1;
+    constexpr int MODE = (SM == SM_NONE || SM == SM_BIAS) ? 0 : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
     bf16x8 pb[QB][NPS];
     if constexpr (SM == SM_NONE || SM == SM_BIAS) {
       // Optimistic: exponentiate against the current reference and keep the
@@ -320,15 +353,15 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       bool redo = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+        tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], cexp, st[qb].m_sub, pb[qb]);
         redo |= (tsum[qb] > kOptBound) || (st[qb].m_ref == neg_inf());
       }
       if (any_lane(redo)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const float rmax = xhalf_max(block_max<NKB>(s[qb]));
-          st[qb].template raise<NDB>(SM == SM_NONE ? rmax * a.c : rmax, o[qb]);
-          tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+          st[qb].template raise<NDB>(rmax * cexp, o[qb]);
+          tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], cexp, st[qb].m_sub, pb[qb]);
         }
       }
 #pragma unroll
@@ -337,9 +370,31 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       // ALiBi scores can climb along the row, so the tile max is tracked
       // with the lazy rescale (one wave-uniform decision for all blocks; each
       // lane tests its own half of the row, the raise uses the whole row).
+      // ALiBi scores already hold the exponent argument relative to the
+      // reference, so the test is against kLazyTau and a raise shifts them.
       // A softcap with a small cap has bounded scores: its reference sits at
       // the cap and no max is taken.
-      if constexpr (SM != SM_SOFTCAP_FIXED) {
+      if constexpr (SM == SM_ALIBI) {
+        float hmax[QB];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          hmax[qb] = block_max<NKB>(s[qb]);
+          grow |= (hmax[qb] > kLazyTau) || (st[qb].m_ref == neg_inf());
+        }
+        if (any_lane(grow)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float old_sub = st[qb].m_sub;
+            st[qb].template raise<NDB>(old_sub + xhalf_max(hmax[qb]), o[qb]);
+            const float shift = st[qb].m_sub - old_sub;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) s[qb][kb][j] -= shift;
+          }
+        }
+      } else if constexpr (SM != SM_SOFTCAP_FIXED) {
         float hmax[QB];
         bool grow = false;
 #pragma unroll
@@ -368,6 +423,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   };
 
   if (n_lo < n_hi) gload(n_lo);
+  if constexpr (SM == SM_BIAS) {
+    if (n_lo < n_hi) bias_load(n_lo * BN);
+  }
 
   for (int nt = n_lo; nt < n_hi; ++nt) {
     const int buf = (nt - n_lo) & 1;
@@ -407,13 +465,12 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     if constexpr (SM == SM_BIAS) {
       // Evoformer: out[b, q, hq*D + d] = sigmoid(gate[b, hq, q, d]) * O[d] / l
       bf16* orow = (bf16*)a.o + ((size_t)b * a.Sq + q) * (size_t)(a.Hq * D) + (size_t)hq * D;
-      const bf16* grow = (const bf16*)a.gate + qoff + (size_t)q * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d0 = db * 32 + 8 * g4 + 4 * hh;
-          const bf16x4 gv = *(const bf16x4*)(grow + d0);
+          const bf16x4 gv = gate[qb][db * 4 + g4];
           bf16x4 val;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {

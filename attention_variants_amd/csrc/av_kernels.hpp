@@ -39,13 +39,14 @@ struct AttnArgs {
 
 // Query rows per workgroup: the differential kernel uses 4 waves x 32 rows;
 // the fused attention kernel uses 4 waves x 32*QB rows, QB = query blocks per
-// wave: 2 at D <= 64, so every K/V fragment read from LDS feeds two MFMAs;
-// 1 at D = 128 (two blocks do not fit the register file) and for the sliding
-// window and document masks, whose short per-row key ranges favour more,
-// smaller workgroups.
+// wave: 2 at D = 64, so every K/V fragment read from LDS feeds two MFMAs;
+// 1 at D = 128 (two blocks do not fit the register file), at D = 32 (the
+// Evoformer shapes: short rows, where more and smaller workgroups hide the
+// load latency better) and for the sliding window and document masks, whose
+// short per-row key ranges favour more, smaller workgroups.
 constexpr int kAttnBM = 128;
 constexpr int attn_qb(int D, int mask) {
-  return (D <= 64 && mask != MK_WINDOW && mask != MK_DOC) ? 2 : 1;
+  return (D == 64 && mask != MK_WINDOW && mask != MK_DOC) ? 2 : 1;
 }
 constexpr int attn_bm(int D, int mask) { return 4 * 32 * attn_qb(D, mask); }
 constexpr int kAttnBMMax = 256;

@@ -112,26 +112,49 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
     }
   }
 
-  // C^T block: lane holds token l32 of the block, channels 8*(j/4) + 4*hh + j%4
-  const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
-  bf16* out = (bf16*)a.ws + (size_t)p * plane;
+  // Epilogue through LDS: the 128 x 128 bf16 C tile is staged token-major
+  // (row pitch CP keeps rows 16-byte aligned; the 32 tokens of one 8-byte
+  // write spread over the banks with at most 2-way conflicts), then written
+  // out as 16-byte chunks.  In the head-major planes the 32
+  // channels of one head are 64 contiguous bytes per token, so consecutive
+  // tokens of one head form one contiguous run.
+  constexpr int CP = GN + 8;
+  static_assert(GM * CP * 2 <= (int)sizeof(Ms), "C tile does not fit the m staging buffers");
+  __syncthreads();  // every wave is done with Ms / Ws
+  bf16* Cs = &Ms[0][0];
 #pragma unroll
   for (int mb2 = 0; mb2 < 2; ++mb2) {
-    const int tok = mt * GM + wm * 64 + mb2 * 32 + l32;
-    if (tok >= M) continue;
-    const int sq = tok / a.Nr, ri = tok % a.Nr;
+    const int tl = wm * 64 + mb2 * 32 + l32;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ch = c0 + wn * 64 + nb * 32 + 8 * g4 + 4 * hh;  // channel within the projection
-        const int h = ch / a.dh, e = ch % a.dh;
         bf16x4 val;
 #pragma unroll
         for (int q = 0; q < 4; ++q) val[q] = (bf16)acc[nb][mb2][g4 * 4 + q];
-        *(bf16x4*)(out + (((size_t)sq * a.H + h) * a.Nr + ri) * a.dh + e) = val;
+        *(bf16x4*)&Cs[tl * CP + wn * 64 + nb * 32 + 8 * g4 + 4 * hh] = val;
       }
     }
+  }
+  __syncthreads();
+  const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
+  bf16* out = (bf16*)a.ws + (size_t)p * plane;
+  constexpr int CPT = 4;                 // 16-byte chunks per token and head (dh = 32: 64 bytes)
+  constexpr int HPT = GN / 32;           // heads per channel tile
+  constexpr int NCHUNK = GM * HPT * CPT / NT;
+  static_assert(GM * HPT * CPT % NT == 0, "chunk/thread mismatch");
+  const int h0 = c0 / 32;
+#pragma unroll
+  for (int k = 0; k < NCHUNK; ++k) {
+    const int id = tid + NT * k;
+    const int hl = id / (GM * CPT);
+    const int rem = id % (GM * CPT);
+    const int tl = rem >> 2, e8 = rem & 3;
+    const int tok = mt * GM + tl;
+    if (tok >= M) continue;
+    const int sq = tok / a.Nr, ri = tok % a.Nr;
+    const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * 32 + e8 * 8];
+    *(i32x4*)(out + (((size_t)sq * a.H + h0 + hl) * a.Nr + ri) * a.dh + e8 * 8) = v;
   }
 }
 

@@ -315,7 +315,7 @@ def run_sweep(path, steps, warmup):
     f.close()
 
 
-def run_profile(what, steps):
+def run_profile(what, steps, nres=256):
     """Launch one kernel `steps` times with nothing else on the stream."""
     import torch
 
@@ -334,7 +334,7 @@ def run_profile(what, steps):
 
     av.load_library()
     if what == "evoformer":
-        Ns, Nr, Cm, Hh, dh = 128, 256, 256, 8, 32
+        Ns, Nr, Cm, Hh, dh = 128, nres, 256, 8, 32
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
         t = {n: _dev(x[n], dev) for n in x}
         ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
@@ -375,6 +375,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "diff"], default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
@@ -388,7 +389,7 @@ def main():
         run_sweep(args.sweep, args.steps, args.warmup)
         return
     if args.profile:
-        run_profile(args.profile, args.steps)
+        run_profile(args.profile, args.steps, args.nres)
         return
     rec = run_headline(args)
     print(json.dumps(rec), flush=True)

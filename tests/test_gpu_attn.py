@@ -146,6 +146,36 @@ def test_reductions_on_gpu(gpu_lib):
     assert (a - c).abs().max().item() < 2e-2
 
 
+def _ramp_inputs(B, H, S, D, q_val, k_step, descending=False):
+    """q = q_val everywhere; key j = (j * k_step) in every column (bf16-rounded),
+    so raw scores grow (or shrink) linearly along the row; V random."""
+    x = wi.attention_inputs(B, H, H, S, S, D)
+    j = np.arange(S, dtype=np.float32)
+    if descending:
+        j = j[::-1].copy()
+    krow = wi.bf16_bits_from_f32(j * np.float32(k_step))
+    k = np.broadcast_to(krow[None, None, :, None], (B, H, S, D)).copy()
+    q = np.broadcast_to(wi.bf16_bits_from_f32(np.float32(q_val)), (B, H, S, D)).copy()
+    return q, k, x["v"]
+
+
+@pytest.mark.parametrize("descending", [False, True])
+@pytest.mark.parametrize("score_mod", SCORE_MODS)
+def test_rising_and_falling_scores(gpu_lib, score_mod, descending):
+    """Scores that climb by ~185 (log2 units) per 64-key tile force the
+    exponent reference up on every tile (without the raise the exponentials
+    would overflow); falling scores keep the first tile's reference."""
+    B, H, S, D = 1, 2, 300, 64
+    q, k, v = _ramp_inputs(B, H, S, D, 8.0, 1.0 / 32, descending)
+    for mask in ("none", "causal"):
+        out, lse = gpu_lib.attn_fwd(to_dev(q), to_dev(k), to_dev(v), score_mod=score_mod, mask=mask, return_lse=True)
+        torch.cuda.synchronize()
+        ref, ref_lse = oracle.attention(f64(q), f64(k), f64(v), score_mod=score_mod, mask=mask)
+        what = f"ramp {score_mod}/{mask} desc={descending}"
+        assert_close(out.float().cpu().numpy(), ref, what)
+        assert_close(lse.cpu().numpy(), ref_lse, what + " lse", atol=LSE_ATOL, rtol=1e-5)
+
+
 def test_deterministic(gpu_lib):
     B, H, S, D = 2, 4, 1000, 64
     x = wi.attention_inputs(B, H, H, S, S, D)
