@@ -18,4 +18,5 @@ from .attention import (  # noqa: F401
     sigmoid,
     evoformer_projections,
     evoformer_row_gated_attention,
+    evoformer_col_gated_attention,
 )

@@ -263,3 +263,37 @@ def evoformer_row_gated_attention(m, wq, wk, wv, wg, bias, *, H: int, dh: int,
             p, _ = softmax_two_pass(s, everything)
             out[si, :, c] = sigmoid(g[si, rows, c]) * (p @ v[si, :, c])
     return out
+
+
+def evoformer_col_gated_attention(m, wq, wk, wv, wg, *, H: int, dh: int,
+                                  scale: float | None = None, cols=None, seqs=None):
+    """Column-wise gated self-attention of the Evoformer MSA stack.
+
+    The pages name the row- and column-wise gated self-attention of
+    AlphaFold2's Evoformer together (talk notes "Flashlight: PyTorch Compiler
+    Extensions to Accelerate Attention Variants", background and the
+    complex-variant evaluation) and give no formula.  Reading: the same four
+    projections of the MSA representation as the row-wise form; for every
+    residue column r and head h, softmax attention over the N_seq sequences
+    of that column (no pair bias), gated by sigmoid(m Wg), channels head-major.
+
+    m [Ns, Nr, Cm], w* [Cm, H*dh] -> out [len(seqs), len(cols), H*dh].
+    """
+    m = np.asarray(m, dtype=np.float64)
+    Ns, Nr, _ = m.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    cols = np.arange(Nr) if cols is None else np.asarray(cols, dtype=np.int64)
+    seqs = np.arange(Ns) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    mc = m[:, cols]                                   # every sequence of the chosen columns
+    q, k, v, g = evoformer_projections(mc, wq, wk, wv, wg)
+    out = np.zeros((len(seqs), len(cols), H * dh))
+    everything = np.ones((len(seqs), Ns), dtype=bool)
+    for ci in range(len(cols)):
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            s = raw_scores(q[seqs, ci, c], k[:, ci, c], scale)
+            p, _ = softmax_two_pass(s, everything)
+            out[:, ci, c] = sigmoid(g[seqs, ci, c]) * (p @ v[:, ci, c])
+    return out
+

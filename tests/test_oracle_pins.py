@@ -408,6 +408,39 @@ def test_p8_evoformer_reductions():
     np.testing.assert_allclose(part, base[[2]][:, [0, 5, 10]], rtol=0, atol=1e-12)
 
 
+def test_p8_evoformer_column_pins():
+    """Column-wise form: every column equals the row-wise form applied to
+    the transposed MSA with a zero bias; one sequence gives sigmoid(g) * v;
+    zero gate weights halve it; a scalar loop agrees; sampling is exact."""
+    Ns, Nr, Cm, H, dh = 5, 4, 16, 2, 4
+    m = _rand((Ns, Nr, Cm), 40)
+    wq, wk, wv, wg = (_rand((Cm, H * dh), 41 + i) / 4 for i in range(4))
+    col = oracle.evoformer_col_gated_attention(m, wq, wk, wv, wg, H=H, dh=dh)
+    assert col.shape == (Ns, Nr, H * dh)
+    mt = m.transpose(1, 0, 2)
+    row_t = oracle.evoformer_row_gated_attention(mt, wq, wk, wv, wg, np.zeros((H, Ns, Ns)), H=H, dh=dh)
+    np.testing.assert_allclose(col, row_t.transpose(1, 0, 2), rtol=0, atol=1e-12)
+    # a single sequence attends only to itself
+    one = oracle.evoformer_col_gated_attention(m[:1], wq, wk, wv, wg, H=H, dh=dh)
+    g = m[0] @ wg
+    np.testing.assert_allclose(one[0], (1 / (1 + np.exp(-g))) * (m[0] @ wv), rtol=0, atol=1e-12)
+    # zero gate weights: half of the ungated attention, checked by a scalar loop
+    half = oracle.evoformer_col_gated_attention(m, wq, wk, wv, np.zeros_like(wg), H=H, dh=dh)
+    for r in range(Nr):
+        q, k, v = m[:, r] @ wq, m[:, r] @ wk, m[:, r] @ wv
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            for i in range(Ns):
+                z = [float(q[i, c] @ k[j, c]) / math.sqrt(dh) for j in range(Ns)]
+                zm = max(z)
+                e = [math.exp(t - zm) for t in z]
+                want = sum(e[j] * v[j, c] for j in range(Ns)) / sum(e)
+                np.testing.assert_allclose(half[i, r, c], 0.5 * want, rtol=0, atol=1e-12)
+    part = oracle.evoformer_col_gated_attention(m, wq, wk, wv, wg, H=H, dh=dh, cols=np.array([3, 1]),
+                                                seqs=np.array([0, 4]))
+    np.testing.assert_allclose(part, col[[0, 4]][:, [3, 1]], rtol=0, atol=1e-12)
+
+
 def _evo_ungated(m, wq, wk, wv, bias, H, dh):
     """Independent loop form: per sequence, head and row."""
     Ns, Nr, _ = m.shape
