@@ -37,6 +37,7 @@ EXPORTED = (
     "diff_attn_fwd",
     "evoformer_workspace_bytes",
     "evoformer_gated_attn_fwd",
+    "evoformer_col_gated_attn_fwd",
     "av_status_string",
     "av_abi_version",
 )
@@ -83,6 +84,9 @@ def load_library(path: str | None = None):
     lib.evoformer_gated_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                              _i, _i, _i, _i, _i, _f, _vp]
     lib.evoformer_gated_attn_fwd.restype = _i
+    lib.evoformer_col_gated_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                                 _i, _i, _i, _i, _i, _f, _vp]
+    lib.evoformer_col_gated_attn_fwd.restype = _i
     lib.av_status_string.argtypes = [_i]
     lib.av_status_string.restype = ctypes.c_char_p
     lib.av_abi_version.argtypes = []
@@ -218,3 +222,33 @@ def evoformer_gated_attn_fwd(m, wq, wk, wv, wg, bias, *, H, dh, scale=0.0, works
                                       Ns, Nr, Cm, H, dh, float(scale or 0.0), _stream_ptr(m.device))
     _check(rc, "evoformer_gated_attn_fwd")
     return out
+
+
+def evoformer_col_gated_attn_fwd(m, wq, wk, wv, wg, *, H, dh, scale=0.0, workspace=None, out=None):
+    """Evoformer column-wise gated self-attention (over the sequences of each
+    residue column, no pair bias).
+
+    m [Ns,Nr,Cm], w* [Cm,H*dh] bf16 -> out [Ns,Nr,H*dh] bf16.
+    ``workspace`` (uint8 device tensor) is allocated when not given.
+    """
+    import torch
+
+    lib = load_library()
+    _need(m, "m", torch.bfloat16, 3)
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
+        _need(t, n, torch.bfloat16, 2)
+    Ns, Nr, Cm = m.shape
+    for t in (wq, wk, wv, wg):
+        if tuple(t.shape) != (Cm, H * dh):
+            raise ValueError("projection weights must be [Cm, H*dh]")
+    need = evoformer_workspace_bytes(Ns, Nr, H, dh)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=m.device)
+    if out is None:
+        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=m.device)
+    rc = lib.evoformer_col_gated_attn_fwd(m.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wg.data_ptr(),
+                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                          Ns, Nr, Cm, H, dh, float(scale or 0.0), _stream_ptr(m.device))
+    _check(rc, "evoformer_col_gated_attn_fwd")
+    return out
+

@@ -152,8 +152,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
   // Evoformer gate pre-activations of this lane's output channels, loaded
   // up front so that their latency hides behind the KV loop
-  bf16x4 gate[QB][SM == SM_BIAS ? NDB * 4 : 1];
-  if constexpr (SM == SM_BIAS) {
+  constexpr bool kGated = SM == SM_BIAS || SM == SM_GATE;
+  bf16x4 gate[QB][kGated ? NDB * 4 : 1];
+  if constexpr (kGated) {
     const auto grs = make_rsrc((const bf16*)a.gate + qoff, (uint32_t)a.Sq * D * 2);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     for (int qb = 0; qb < QB; ++qb) {
       // ---- score modifier: ALiBi and softcap in log2 units, pair bias in natural
       //      units (q.k*scale + bias); vanilla keeps the raw q.k, its scale folded into exp2
-      if constexpr (SM != SM_NONE) {
+      if constexpr (SM != SM_NONE && SM != SM_GATE) {
         // ALiBi goes straight to the exponent argument, relative to the
         // current reference: s*c + slope*(key - query) - m_sub
         float ab[4];
@@ -341,9 +342,10 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
     // ---- exponent reference and p = exp2(t - m_ref) -> bf16 P^T operands,
     //      with the row sum of the bf16 values
-    constexpr int MODE = (SM == SM_NONE || SM == SM_BIAS) ? 0 : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
+    constexpr int MODE = (SM == SM_NONE || SM == SM_BIAS || SM == SM_GATE) ? 0
+                         : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
     bf16x8 pb[QB][NPS];
-    if constexpr (SM == SM_NONE || SM == SM_BIAS) {
+    if constexpr (SM == SM_NONE || SM == SM_BIAS || SM == SM_GATE) {
       // Optimistic: exponentiate against the current reference and keep the
       // result unless some exponential exceeds 2^64 (then the tile sum does)
       // or the row has no reference yet.  The reference is only ever a
@@ -462,9 +464,12 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int q = qi[qb];
     if (q >= a.Sq) continue;
-    if constexpr (SM == SM_BIAS) {
-      // Evoformer: out[b, q, hq*D + d] = sigmoid(gate[b, hq, q, d]) * O[d] / l
-      bf16* orow = (bf16*)a.o + ((size_t)b * a.Sq + q) * (size_t)(a.Hq * D) + (size_t)hq * D;
+    if constexpr (kGated) {
+      // Evoformer: out[token, hq*D + d] = sigmoid(gate[b, hq, q, d]) * O[d] / l with
+      // token = (b, q) row-wise (b sequence, q residue) and (q, b) column-wise
+      // (b residue column, q sequence)
+      const size_t tok = SM == SM_BIAS ? (size_t)b * a.Sq + q : (size_t)q * a.B + b;
+      bf16* orow = (bf16*)a.o + tok * (size_t)(a.Hq * D) + (size_t)hq * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -531,7 +536,9 @@ hipError_t launch_sm(const AttnArgs& a, int sm, int mask, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_evo_attention(const AttnArgs& a, hipStream_t stream) { return launch_one<32, SM_BIAS, MK_NONE>(a, stream); }
+hipError_t launch_evo_attention(const AttnArgs& a, int col, hipStream_t stream) {
+  return col ? launch_one<32, SM_GATE, MK_NONE>(a, stream) : launch_one<32, SM_BIAS, MK_NONE>(a, stream);
+}
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream) {
   switch (D) {

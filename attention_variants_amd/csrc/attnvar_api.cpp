@@ -136,20 +136,26 @@ size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh) {
   return av::evo_workspace_bytes(Ns, Nr, H, dh);
 }
 
-int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
-                             const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr,
-                             int Cm, int H, int dh, float scale, hipStream_t stream) {
-  if (m == nullptr || wq == nullptr || wk == nullptr || wv == nullptr || wg == nullptr || bias == nullptr ||
-      out == nullptr)
+}  // extern "C"
+
+namespace {
+
+// Shared validation and launch of both Evoformer forms (bias == nullptr and
+// col == 1 for the column-wise form).
+int evoformer_launch(const void* m, const void* wq, const void* wk, const void* wv, const void* wg, const void* bias,
+                     void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr, int Cm, int H, int dh,
+                     float scale, int col, hipStream_t stream) {
+  if (m == nullptr || wq == nullptr || wk == nullptr || wv == nullptr || wg == nullptr || out == nullptr ||
+      (!col && bias == nullptr))
     return AV_ERR_NULL;
   if (Ns <= 0 || Nr <= 0 || Cm <= 0 || H <= 0 || dh <= 0) return AV_ERR_SHAPE;
   if (dh != 32 || Cm % 64 != 0 || (H * dh) % 128 != 0) return AV_ERR_UNSUPPORTED;
   if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
   if (!aligned(m, 16) || !aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(wg, 16) ||
-      !aligned(bias, 16) || !aligned(out, 16))
+      (!col && !aligned(bias, 16)) || !aligned(out, 16))
     return AV_ERR_ALIGN;
   if ((uint64_t)Ns * Nr * Cm * 2 > kMaxSliceBytes || (uint64_t)Ns * Nr * H * dh * 2 > kMaxSliceBytes ||
-      (uint64_t)H * Nr * Nr * 2 > kMaxSliceBytes)
+      (!col && (uint64_t)H * Nr * Nr * 2 > kMaxSliceBytes))
     return AV_ERR_TOO_LARGE;
   const size_t need = av::evo_workspace_bytes(Ns, Nr, H, dh);
   if (workspace == nullptr || workspace_bytes < need) return AV_ERR_WORKSPACE;
@@ -160,7 +166,7 @@ int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, cons
   a.w[1] = wk;
   a.w[2] = wv;
   a.w[3] = wg;
-  a.bias = bias;
+  a.bias = col ? nullptr : bias;
   a.out = out;
   a.ws = workspace;
   a.Ns = Ns;
@@ -168,9 +174,28 @@ int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, cons
   a.Cm = Cm;
   a.H = H;
   a.dh = dh;
+  a.col = col;
   const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)dh);
   a.c = (float)(sc * kLog2e);
   return hip_status(av::launch_evoformer(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
+                             const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr,
+                             int Cm, int H, int dh, float scale, hipStream_t stream) {
+  return evoformer_launch(m, wq, wk, wv, wg, bias, out, workspace, workspace_bytes, Ns, Nr, Cm, H, dh, scale, 0,
+                          stream);
+}
+
+int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
+                                 void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr, int Cm, int H,
+                                 int dh, float scale, hipStream_t stream) {
+  return evoformer_launch(m, wq, wk, wv, wg, nullptr, out, workspace, workspace_bytes, Ns, Nr, Cm, H, dh, scale, 1,
+                          stream);
 }
 
 }  // extern "C"

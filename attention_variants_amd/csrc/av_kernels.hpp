@@ -9,9 +9,11 @@ namespace av {
 
 // Internal score modifiers: SM_BIAS = Evoformer pair bias added to the scaled
 // score, with the sigmoid-gate epilogue and a token-major [B, Sq, Hq*D]
-// output; SM_SOFTCAP_FIXED = softcap whose exponent reference is fixed at the
-// cap (chosen by the launcher when fixed_ref is set).
-enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3, SM_SOFTCAP_FIXED = 4 };
+// output (row-wise form); SM_GATE = no modifier, sigmoid-gate epilogue and a
+// token-major [Sq, B, Hq*D] output (column-wise form: problem b is residue
+// column b, query q is sequence q); SM_SOFTCAP_FIXED = softcap whose exponent
+// reference is fixed at the cap (chosen by the launcher when fixed_ref is set).
+enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3, SM_SOFTCAP_FIXED = 4, SM_GATE = 5 };
 enum MaskKind : int { MK_NONE = 0, MK_CAUSAL = 1, MK_WINDOW = 2, MK_PREFIX = 3, MK_DOC = 4 };
 
 // Kernel argument block of the fused attention forward (passed by value).
@@ -52,8 +54,9 @@ constexpr int attn_bm(int D, int mask) { return 4 * 32 * attn_qb(D, mask); }
 constexpr int kAttnBMMax = 256;
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
-// Evoformer gated attention over the projected workspace (D = 32, SM_BIAS).
-hipError_t launch_evo_attention(const AttnArgs& a, hipStream_t stream);
+// Evoformer gated attention over the projected workspace (D = 32): row-wise
+// (SM_BIAS) or column-wise (SM_GATE).
+hipError_t launch_evo_attention(const AttnArgs& a, int col, hipStream_t stream);
 
 struct DiffArgs {
   const void* q;
@@ -73,8 +76,9 @@ struct EvoArgs {
   const void* w[4];  // wq, wk, wv, wg  [Cm, H*dh]
   const void* bias;  // [H, Nr, Nr]
   void* out;         // [Ns, Nr, H*dh]
-  void* ws;          // 4 x [Ns, H, Nr, dh] bf16
+  void* ws;          // 4 planes (q, k, v, g) bf16: [Ns, H, Nr, dh] row-wise, [Nr, H, Ns, dh] column-wise
   int Ns, Nr, Cm, H, dh;
+  int col;           // 0: row-wise (pair bias), 1: column-wise (no bias)
   float c;           // scale * log2(e)
 };
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh);

@@ -19,6 +19,11 @@
 //     modifier and the sigmoid gate + token-major store as epilogue; each
 //     (sequence, head, 128-residue tile) is one workgroup, sequences vary
 //     fastest within a head so bias[h] stays resident in L2.
+//
+// The column-wise form (attention over the sequences of each residue column,
+// no pair bias) runs the same two launches: the GEMM orders tokens column-
+// major and writes planes [Nr, H, Ns, dh], and the attention kernel takes one
+// (residue, head) per problem with the gated epilogue only.
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
@@ -50,9 +55,25 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
   const int c0 = n0 % HD;
   const int wn = w & 1, wm = w >> 1;           // wave: 64 channels x 64 tokens
 
-  const auto mrs = make_rsrc((const bf16*)a.m + (size_t)mt * GM * a.Cm, (uint32_t)min(GM, M - mt * GM) * a.Cm * 2);
+  // Token order: row-wise, token t = (sequence, residue) in MSA order; column-
+  // wise, t = residue * Ns + sequence, so that the tokens of one attention
+  // problem (one residue column) are consecutive.  Linner is the attention
+  // length, the inner factor of t.
+  const int Linner = a.col ? a.Ns : a.Nr;
+  const uint32_t m_bytes = (uint32_t)M * a.Cm * 2;
+  const auto mrs = make_rsrc(a.m, m_bytes);
   const bf16* wbase = (const bf16*)a.w[p];
   const auto wrs = make_rsrc(wbase, (uint32_t)a.Cm * HD * 2);
+
+  // byte offset of the m row of each token this thread stages (past the end:
+  // tokens beyond M, read as zeros)
+  uint32_t mrow_off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int t = mt * GM + ((tid + NT * c) >> 3);
+    const int row = a.col ? (t % a.Ns) * a.Nr + t / a.Ns : t;
+    mrow_off[c] = t < M ? (uint32_t)row * a.Cm * 2 : m_bytes;
+  }
 
   // staging: m chunk 128 x 64 and W chunk 64 x 128, 4 x 16 bytes per thread each
   i32x4 mr[4], wr[4];
@@ -60,8 +81,8 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int idx = tid + NT * c;
-      const int mrow = idx >> 3, mcol = idx & 7;
-      mr[c] = buf_load16(mrs, (uint32_t)(mrow * a.Cm + kc * GK + mcol * 8) * 2);
+      const int mcol = idx & 7;
+      mr[c] = buf_load16(mrs, mrow_off[c] + (uint32_t)(kc * GK + mcol * 8) * 2);
       const int wrow = idx >> 4, wcol = idx & 15;
       wr[c] = buf_load16(wrs, (uint32_t)((kc * GK + wrow) * HD + c0 + wcol * 8) * 2);
     }
@@ -152,9 +173,9 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
     const int tl = rem >> 2, e8 = rem & 3;
     const int tok = mt * GM + tl;
     if (tok >= M) continue;
-    const int sq = tok / a.Nr, ri = tok % a.Nr;
+    const int outer = tok / Linner, inner = tok % Linner;
     const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * 32 + e8 * 8];
-    *(i32x4*)(out + (((size_t)sq * a.H + h0 + hl) * a.Nr + ri) * a.dh + e8 * 8) = v;
+    *(i32x4*)(out + (((size_t)outer * a.H + h0 + hl) * Linner + inner) * a.dh + e8 * 8) = v;
   }
 }
 
@@ -169,6 +190,10 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  // attention problems: row-wise, one per (sequence, head) over the residues;
+  // column-wise, one per (residue, head) over the sequences
+  const int nB = a.col ? a.Nr : a.Ns;
+  const int L = a.col ? a.Ns : a.Nr;
   const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
   const bf16* ws = (const bf16*)a.ws;
   AttnArgs t{};
@@ -179,17 +204,17 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   t.o = a.out;
   t.lse = nullptr;
   t.doc = nullptr;
-  t.bias = a.bias;
-  t.B = a.Ns;
+  t.bias = a.col ? nullptr : a.bias;
+  t.B = nB;
   t.Hq = t.Hkv = a.H;
-  t.Sq = t.Skv = a.Nr;
+  t.Sq = t.Skv = L;
   t.g = 1;
-  t.nM = (a.Nr + attn_bm(32, MK_NONE) - 1) / attn_bm(32, MK_NONE);
-  t.total = a.Ns * a.H * t.nM;
+  t.nM = (L + attn_bm(32, MK_NONE) - 1) / attn_bm(32, MK_NONE);
+  t.total = nB * a.H * t.nM;
   t.c = a.c;
   t.scale = a.c / 1.4426950408889634f;
   t.softcap = 1.f;
-  return launch_evo_attention(t, stream);
+  return launch_evo_attention(t, a.col, stream);
 }
 
 }  // namespace av

@@ -312,6 +312,14 @@ def run_sweep(path, steps, warmup):
         tf = fl / (per[0] * 1e-3) / 1e12
         emit({"kernel": "evoformer_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        # column-wise form on the same MSA: attention over the 128 sequences of each residue column
+        _, per = time_launches([lambda: av.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"],
+                                                                        H=Hh, dh=dh, workspace=ws, out=out)],
+                               steps, warmup)
+        fl = 2 * Ns * Nr * Cm * 4 * Hh * dh + 4 * Nr * Hh * Ns * Ns * dh
+        tf = fl / (per[0] * 1e-3) / 1e12
+        emit({"kernel": "evoformer_col_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "us": round(per[0] * 1e3, 2),
+              "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
     f.close()
 
 
@@ -346,6 +354,19 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "evoformer", "Ns": Ns, "Nr": Nr, "launches": steps}))
         return
+    if what == "evoformer_col":
+        Ns, Nr, Cm, Hh, dh = 128, nres, 256, 8, 32
+        x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
+        t = {n: _dev(x[n], dev) for n in x}
+        ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
+        out = torch.empty((Ns, Nr, Hh * dh), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], H=Hh, dh=dh,
+                                            workspace=ws, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "evoformer_col", "Ns": Ns, "Nr": Nr, "launches": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -377,7 +398,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
-    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "diff"], default=None,
+    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff"],
+                    default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()

@@ -133,6 +133,21 @@ int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, cons
                              const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns,
                              int Nr, int Cm, int H, int dh, float scale, hipStream_t stream);
 
+/* Evoformer column-wise gated self-attention (the sibling the pages name with
+ * the row-wise form: talk notes "Background and motivation" and "Evaluation:
+ * complex attention variants"; no formula on the pages; the reading
+ * implemented is, per residue column r, head h, sequences s, t):
+ *   q, k, v, g = m Wq, m Wk, m Wv, m Wg                 (the same projections)
+ *   out[s, r, h*dh + e] = sigmoid(g[s, r, h*dh + e])
+ *                         * sum_t softmax_t(scale * q[s, r].k[t, r]) v[t, r][e]
+ *   m    [Ns, Nr, Cm]      w* [Cm, H*dh] each      (no pair bias)
+ *   out  [Ns, Nr, H*dh]
+ * Workspace, scale, supported shapes and errors as evoformer_gated_attn_fwd;
+ * the workspace size is the same (evoformer_workspace_bytes). */
+int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
+                                 void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr, int Cm, int H,
+                                 int dh, float scale, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* av_status_string(int status);
 

@@ -136,6 +136,26 @@ def test_evoformer_rejections(lib):
     assert call(ws=0x100000 + 16) == -4
 
 
+def test_evoformer_column_rejections(lib):
+    def call(m=P, w=P2, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):
+        if wsb is None:
+            wsb = lib.evoformer_workspace_bytes(max(Ns, 1), max(Nr, 1), max(H, 1), max(dh, 1))
+        return lib.evoformer_col_gated_attn_fwd(m, w, w, w, w, out, ws, wsb, Ns, Nr, Cm, H, dh, scale, None)
+
+    assert call(m=None) == -1
+    assert call(w=None) == -1
+    assert call(out=None) == -1
+    assert call(Nr=0) == -2
+    assert call(dh=16) == -3
+    assert call(Cm=96) == -3
+    assert call(H=1) == -3
+    assert call(scale=float("inf")) == -7
+    assert call(out=P4 + 8) == -4
+    assert call(ws=None) == -5
+    assert call(wsb=1) == -5
+    assert call(ws=0x100000 + 128) == -4
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
 
