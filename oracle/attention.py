@@ -116,10 +116,12 @@ def softmax_two_pass(s: np.ndarray, allowed: np.ndarray):
     return p, lse
 
 
-def _head_probs(qh, kh, rows, *, scale, score_mod, mask, slope, softcap, window, prefix_len, doc_row):
+def _head_probs(qh, kh, rows, *, scale, score_mod, mask, slope, softcap, window, prefix_len, doc_row,
+                q_offset=0):
     s = raw_scores(qh[rows], kh, scale)
-    s = apply_score_mod(s, score_mod, rows, np.arange(kh.shape[0]), slope=slope, softcap=softcap)
-    a = allowed_matrix(mask, rows, kh.shape[0], window=window, prefix_len=prefix_len, doc_row=doc_row)
+    pos = rows + q_offset  # absolute position of each query row
+    s = apply_score_mod(s, score_mod, pos, np.arange(kh.shape[0]), slope=slope, softcap=softcap)
+    a = allowed_matrix(mask, pos, kh.shape[0], window=window, prefix_len=prefix_len, doc_row=doc_row)
     return softmax_two_pass(s, a)
 
 
@@ -138,12 +140,17 @@ def attention(
     doc_id=None,
     rows=None,
     row_block: int = 1024,
+    q_offset: int = 0,
 ):
     """out = softmax(mask(score_mod(scale * Q K^T))) V, per (batch, query head).
 
     GQA reading: query head ``hq`` reads key/value head ``hq // (Hq // Hkv)``
     (contiguous groups).  ``rows`` restricts the computation to a subset of
     query rows (each row is independent, so a sampled row is exact).
+    ``q_offset`` is the absolute position of query row 0 (ALiBi distances and
+    masks use row + q_offset).  Decoding reading: the Sq queries are the last
+    Sq positions of the Skv keys, q_offset = Skv - Sq; with a mask the queries
+    must end at the last key.
     Returns ``(out, lse)``; ``lse`` is natural-log ``m + ln l`` of the scores
     after score_mod and mask.
     """
@@ -159,8 +166,8 @@ def attention(
         raise ValueError(mask)
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    if mask != "none" and Sq != Skv:
-        raise ValueError("masks need Sq == Skv")
+    if mask != "none" and Sq + q_offset != Skv:
+        raise ValueError("masks need the queries to end at the last key (Sq + q_offset == Skv)")
     g = Hq // Hkv
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -179,6 +186,7 @@ def attention(
                     q[b, hq], k[b, hk], rr,
                     scale=scale, score_mod=score_mod, mask=mask, slope=slope,
                     softcap=softcap, window=window, prefix_len=prefix_len, doc_row=doc_row,
+                    q_offset=q_offset,
                 )
                 out[b, hq, r0 : r0 + len(rr)] = p @ v[b, hk]
                 lse[b, hq, r0 : r0 + len(rr)] = l_

@@ -441,6 +441,47 @@ def test_p8_evoformer_column_pins():
     np.testing.assert_allclose(part, col[[0, 4]][:, [3, 1]], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("score_mod", ["none", "alibi", "softcap"])
+def test_decode_queries_at_the_end(score_mod):
+    """Queries placed at the end of the keys (q_offset = Skv - Sq) equal the
+    last rows of the full prefill; one query under the causal mask equals the
+    unmasked attention of that query; a scalar loop agrees on a tiny case."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 37, 8
+    q = _rand((B, Hq, S, D), 50)
+    k = _rand((B, Hkv, S, D), 51)
+    v = _rand((B, Hkv, S, D), 52)
+    for mask in ("none", "causal"):
+        full, full_lse = oracle.attention(q, k, v, score_mod=score_mod, mask=mask)
+        for Sq in (1, 3, S):
+            dec, dec_lse = oracle.attention(q[:, :, S - Sq:], k, v, score_mod=score_mod, mask=mask, q_offset=S - Sq)
+            np.testing.assert_allclose(dec, full[:, :, S - Sq:], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dec_lse, full_lse[:, :, S - Sq:], rtol=0, atol=1e-12)
+    one_c, _ = oracle.attention(q[:, :, -1:], k, v, score_mod=score_mod, mask="causal", q_offset=S - 1)
+    one_n, _ = oracle.attention(q[:, :, -1:], k, v, score_mod=score_mod, mask="none", q_offset=S - 1)
+    np.testing.assert_allclose(one_c, one_n, rtol=0, atol=1e-12)
+    # scalar loop: two queries at positions 5, 6 over 7 keys, causal
+    qs, ks, vs = q[0, 0, :2], k[0, 0, :7], v[0, 0, :7]
+    dec, _ = oracle.attention(qs[None, None], ks[None, None], vs[None, None], score_mod=score_mod, mask="causal",
+                              q_offset=5)
+    slope = oracle.alibi_slope(0, 1)
+    for i in range(2):
+        pos = 5 + i
+        z = []
+        for j in range(pos + 1):
+            t = float(qs[i] @ ks[j]) / math.sqrt(D)
+            if score_mod == "alibi":
+                t += slope * (j - pos)
+            if score_mod == "softcap":
+                t = 20.0 * math.tanh(t / 20.0)
+            z.append(t)
+        zm = max(z)
+        e = [math.exp(t - zm) for t in z]
+        want = sum(e[j] * vs[j] for j in range(pos + 1)) / sum(e)
+        np.testing.assert_allclose(dec[0, 0, i], want, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.attention(q[:, :, :3], k, v, mask="causal", q_offset=0)
+
+
 def _evo_ungated(m, wq, wk, wv, bias, H, dh):
     """Independent loop form: per sequence, head and row."""
     Ns, Nr, _ = m.shape
