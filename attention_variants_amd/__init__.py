@@ -34,6 +34,8 @@ STATUS = {
 # Names the header declares; tests check that the library exports each one.
 EXPORTED = (
     "attn_fwd",
+    "attn_decode_workspace_bytes",
+    "attn_decode_fwd",
     "diff_attn_fwd",
     "evoformer_workspace_bytes",
     "evoformer_gated_attn_fwd",
@@ -77,6 +79,11 @@ def load_library(path: str | None = None):
     lib = ctypes.CDLL(p)
     lib.attn_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_fwd.restype = _i
+    lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                    _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_decode_fwd.restype = _i
     lib.diff_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp]
     lib.diff_attn_fwd.restype = _i
     lib.evoformer_workspace_bytes.argtypes = [_i, _i, _i, _i]
@@ -167,6 +174,45 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
     rc = lib.attn_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       None if lse is None else lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
     _check(rc, "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D))
+
+
+def attn_decode_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0, alibi_max_bias=8.0,
+                    kv_group=0, return_lse=False, out=None, lse=None, workspace=None):
+    """Decoding / short-query attention: q [B,Hq,Sq,D] are the last Sq positions of
+    k/v [B,Hkv,Skv,D] (bf16) -> out [B,Hq,Sq,D].  Masks: none or causal.
+    ``workspace`` (uint8 device tensor) is allocated when needed and not given.
+    """
+    import torch
+
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) if Sq > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
+                       kv_group=kv_group)
+    rc = lib.attn_decode_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             None if lse is None else lse.data_ptr(),
+                             None if workspace is None else workspace.data_ptr(),
+                             0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, Skv, D,
+                             _stream_ptr(q.device))
+    _check(rc, "attn_decode_fwd")
     return (out, lse) if return_lse else out
 
 

@@ -1,0 +1,322 @@
+// Decoding / short-query attention forward for gfx950 (split-KV).
+//
+// The pages' serving workload runs causal and softcapped LLaMA-3.2-1B
+// variants under vLLM (talk notes "Flashlight: PyTorch Compiler Extensions to
+// Accelerate Attention Variants", end-to-end section, LLaMA-3.2-1B on the
+// Mooncake trace); after prefill, every step attends a few new queries to a
+// long key/value cache.  Reading implemented: the Sq queries of a sequence
+// are the last Sq positions of its Skv keys (absolute position
+// Skv - Sq + q), which is where the causal mask and the ALiBi distances are
+// measured from.  The arithmetic per score is the prefill kernel's (same
+// score modifiers, same exponent-reference schemes, fp32 accumulation).
+//
+// Mapping onto CDNA4 (memory-bound: every K/V byte is read once, the
+// matrix work is small):
+//  * One workgroup = one (batch, KV head, key split).  All g = Hq/Hkv query
+//    heads of the KV head and all Sq queries share one 32-row MFMA block
+//    (g*Sq <= 32 rows), so each K/V byte is read once per KV head.
+//  * The 4 waves take the split's 64-key tiles round-robin and never meet
+//    inside the key loop (no barrier): K goes from memory straight into the
+//    MFMA A-operand registers of S^T = K Q^T, V is staged row-major in a
+//    wave-private LDS slot and read transposed for O^T = V^T P^T.
+//  * At the end the 4 waves merge (m, l, O) through LDS.  With one split the
+//    result is final; with several, each split writes its partial state to
+//    the workspace and a second kernel merges the splits (the same rescale as
+//    the online softmax).
+
+#include <algorithm>
+
+#include "attn_tile.hpp"
+#include "av_kernels.hpp"
+
+namespace av {
+namespace {
+
+constexpr int NT = 256;
+constexpr int BN = 64;   // keys per tile
+constexpr int ROWS = 32; // query rows per workgroup (one MFMA block)
+
+template <int D, int SM, bool CAUSAL>
+__global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) {
+  constexpr int NKB = BN / 32, NDB = D / 32, NDS = D / 16, NPS = BN / 16;
+  constexpr int VCH = BN * D / 8 / 64;  // 16-byte V chunks per lane per tile
+  __shared__ __attribute__((aligned(16))) bf16 Vs[4][BN * D];  // one slot per wave, swizzled
+  __shared__ float Ms[4][ROWS], Ls[4][ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int L = xcd_remap(blockIdx.x, a.total);
+  const int split = L % a.NS;
+  const int bk = L / a.NS;
+  const int hk = bk % a.Hkv, b = bk / a.Hkv;
+
+  // ---- this lane's query row: r -> (head hk*g + r/Sq, query r%Sq)
+  const int R = a.g * a.Sq;
+  const int r = l32;
+  const bool row_live = r < R;
+  const int hq = hk * a.g + (row_live ? r / a.Sq : 0);
+  const int qq = row_live ? r % a.Sq : 0;
+  const int pos = a.Skv - a.Sq + qq;  // absolute position of the query
+  const auto qrs = make_rsrc((const bf16*)a.q + (((size_t)b * a.Hq + hq) * a.Sq + qq) * D,
+                             row_live ? (uint32_t)D * 2 : 0u);
+  bf16x8 qreg[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(s * 16 + hh * 8) * 2));
+
+  const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
+  const auto krs = make_rsrc((const bf16*)a.k + kvoff, (uint32_t)a.Skv * D * 2);
+  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, (uint32_t)a.Skv * D * 2);
+
+  const int nKV = (a.Skv + BN - 1) / BN;
+  const int t_lo = split * a.tps, t_hi = min(nKV, t_lo + a.tps);
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+  RowState st;
+  const TrLane<D> vl(lane);
+  bf16* Vw = Vs[w];
+
+  const float cap2 = a.softcap * kLog2e;
+  const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
+  const float invK = 0.5f / cap2;
+  if constexpr (SM == SM_SOFTCAP_FIXED) st.m_ref = cap2;
+  // per-row ALiBi slope (log2 units); rows of one workgroup span several heads
+  const float slope2 = SM == SM_ALIBI ? kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq) : 0.f;
+
+  for (int t = t_lo + w; t < t_hi; t += 4) {
+    const int n0 = t * BN;
+    // ---- V tile -> registers -> this wave's LDS slot (row-major, swizzled)
+    i32x4 vr[VCH];
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = lane + 64 * c;
+      const int row = idx / (D / 8), col = idx % (D / 8);
+      vr[c] = buf_load16(vrs, (uint32_t)((n0 + row) * D + col * 8) * 2);
+    }
+    // ---- K fragments straight into the A operand: key kb*32 + l32, d = st*16 + 8*hh .. +7
+    bf16x8 kf[NKB][NDS];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
+        kf[kb][s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (uint32_t)((n0 + kb * 32 + l32) * D + s * 16 + hh * 8) * 2));
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = lane + 64 * c;
+      const int row = idx / (D / 8), col = idx % (D / 8);
+      *(i32x4*)&Vw[tr_tile_off<D>(row, col * 8)] = vr[c];
+    }
+
+    // ---- S^T = K Q^T: lane holds keys n0 + kb*32 + 8*(j/4) + 4*hh + j%4 of row r
+    f32x16 s[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int st_ = 0; st_ < NDS; ++st_) s[kb] = mfma32(kf[kb][st_], qreg[st_], s[kb]);
+    }
+    const int kbase = n0 + 4 * hh;
+    // ---- score modifier
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+        if constexpr (SM == SM_ALIBI) {
+          s[kb][j] = fmaf(s[kb][j], a.c, slope2 * (float)(kbase + off - pos));
+        } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+          const float rr = rcp_fast(fmaf(exp2_fast(s[kb][j] * sc_k), invK, invK));
+          s[kb][j] = SM == SM_SOFTCAP_FIXED ? -rr : cap2 - rr;
+        }
+      }
+    // ---- mask: keys past the end, and (causal) keys after the query's position
+    const bool full = (n0 + BN <= a.Skv) && (!CAUSAL || n0 + BN - 1 <= a.Skv - a.Sq);
+    if (!full) {
+      int lim = a.Skv - kbase, rel = pos - kbase;
+      asm volatile("" : "+v"(lim), "+v"(rel));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
+          const bool ok = (off < lim) && (!CAUSAL || off <= rel);
+          s[kb][j] = ok ? s[kb][j] : neg_inf();
+          if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // ---- exponent reference and exponentials (the prefill kernel's schemes)
+    bf16x8 pb[NPS];
+    if constexpr (SM == SM_NONE) {
+      float tsum = exp_pack_sum<NKB, 0>(s, a.c, st.m_sub, pb);
+      if (any_lane(tsum > kOptBound || st.m_ref == neg_inf())) {
+        st.template raise<NDB>(xhalf_max(block_max<NKB>(s)) * a.c, o);
+        tsum = exp_pack_sum<NKB, 0>(s, a.c, st.m_sub, pb);
+      }
+      st.l += tsum;
+    } else if constexpr (SM == SM_SOFTCAP_FIXED) {
+      st.l += exp_pack_sum<NKB, 2>(s, a.c, st.m_sub, pb);
+    } else {  // ALiBi, softcap with a large cap: lazy rescale on the tile max
+      const float hmax = block_max<NKB>(s);
+      if (any_lane(hmax > st.thr)) st.template raise<NDB>(xhalf_max(hmax), o);
+      st.l += exp_pack_sum<NKB, 1>(s, a.c, st.m_sub, pb);
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int tt = 0; tt < NPS; ++tt) o[db] = mfma32(vt_operand<D>(Vw, tt, db * 32, vl), pb[tt], o[db]);
+  }
+
+  // ---- merge the 4 waves: m, l per row, then O through the (now free) V slots
+  const float l_row = xhalf_sum(st.l);
+  __syncthreads();
+  if (hh == 0) {
+    Ms[w][r] = st.m_ref;
+    Ls[w][r] = l_row;
+  }
+  float* Os = (float*)&Vs[0][0];  // [4 waves][ROWS][D] fp32 = 4 * 32 * D * 4 bytes
+  static_assert(4 * ROWS * D * 4 <= (int)sizeof(Vs), "merge buffer does not fit");
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int d = db * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+      Os[(w * ROWS + r) * D + d] = o[db][j];
+    }
+  __syncthreads();
+  // each thread merges ROWS*D/NT elements: row rr, columns dd .. dd+EPT-1
+  constexpr int EPT = ROWS * D / NT;
+  const int rr = tid / (D / EPT);
+  const int dd = (tid % (D / EPT)) * EPT;
+  float mw[4], M = neg_inf();
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    mw[ww] = Ms[ww][rr];
+    M = fmaxf(M, mw[ww]);
+  }
+  const float Msub = M == neg_inf() ? 0.f : M;
+  float f[4], Lsum = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    f[ww] = exp2_fast(mw[ww] - Msub);
+    Lsum = fmaf(Ls[ww][rr], f[ww], Lsum);
+  }
+  float acc[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) x = fmaf(Os[(ww * ROWS + rr) * D + dd + e], f[ww], x);
+    acc[e] = x;
+  }
+  if (rr >= R) return;
+  const int ohq = hk * a.g + rr / a.Sq, oq = rr % a.Sq;
+  const size_t orow = ((size_t)b * a.Hq + ohq) * a.Sq + oq;
+  if (a.NS == 1) {
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4) {
+      bf16x4 val;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) val[q4] = (bf16)(acc[e + q4] * inv);
+      *(bf16x4*)((bf16*)a.o + orow * D + dd + e) = val;
+    }
+    if (a.lse != nullptr && dd == 0) a.lse[orow] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : neg_inf();
+  } else {
+    // partial state of this split: O relative to 2^M, and (M, L)
+    const size_t unit = ((size_t)bk * a.NS + split) * ROWS + rr;
+#pragma unroll
+    for (int e = 0; e < EPT; e += 4)
+      *(f32x4*)(a.ws_o + unit * D + dd + e) = f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    if (dd == 0) {
+      a.ws_ml[unit * 2] = M;
+      a.ws_ml[unit * 2 + 1] = Lsum;
+    }
+  }
+}
+
+// Merge of the key splits: one thread per (row, 4 columns).
+template <int D>
+__global__ __launch_bounds__(NT) void attn_decode_combine(const DecodeArgs a) {
+  const int R = a.g * a.Sq;
+  const long long n = (long long)a.B * a.Hkv * R * (D / 4);
+  const long long i = (long long)blockIdx.x * NT + threadIdx.x;
+  if (i >= n) return;
+  const int d4 = (int)(i % (D / 4));
+  const long long rowi = i / (D / 4);
+  const int rr = (int)(rowi % R);
+  const int bk = (int)(rowi / R);
+  float M = neg_inf();
+  for (int s = 0; s < a.NS; ++s) M = fmaxf(M, a.ws_ml[(((size_t)bk * a.NS + s) * ROWS + rr) * 2]);
+  const float Msub = M == neg_inf() ? 0.f : M;
+  float Lsum = 0.f;
+  f32x4 acc = {};
+  for (int s = 0; s < a.NS; ++s) {
+    const size_t unit = ((size_t)bk * a.NS + s) * ROWS + rr;
+    const float f = exp2_fast(a.ws_ml[unit * 2] - Msub);
+    Lsum = fmaf(a.ws_ml[unit * 2 + 1], f, Lsum);
+    const f32x4 x = *(const f32x4*)(a.ws_o + unit * D + d4 * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], f, acc[e]);
+  }
+  const int hk = bk % a.Hkv, b = bk / a.Hkv;
+  const int ohq = hk * a.g + rr / a.Sq, oq = rr % a.Sq;
+  const size_t orow = ((size_t)b * a.Hq + ohq) * a.Sq + oq;
+  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+  bf16x4 val;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) val[e] = (bf16)(acc[e] * inv);
+  *(bf16x4*)((bf16*)a.o + orow * D + d4 * 4) = val;
+  if (a.lse != nullptr && d4 == 0) a.lse[orow] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : neg_inf();
+}
+
+template <int D, int SM, bool CAUSAL>
+hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_decode_kernel<D, SM, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.NS == 1) return e;
+  const long long n = (long long)a.B * a.Hkv * a.g * a.Sq * (D / 4);
+  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int SM>
+hipError_t launch_dec_mask(const DecodeArgs& a, int causal, hipStream_t stream) {
+  return causal ? launch_dec<64, SM, true>(a, stream) : launch_dec<64, SM, false>(a, stream);
+}
+
+}  // namespace
+
+DecodePlan decode_plan(int B, int Hkv, int Skv) {
+  DecodePlan p{};
+  const int nKV = (Skv + 63) / 64;
+  const int units = B * Hkv;
+  // enough workgroups to fill the chip (3 per CU), and at least 4 tiles
+  // (one per wave) in every split
+  int ns = (768 + units - 1) / units;
+  ns = std::min(ns, std::max(1, nKV / 4));
+  ns = std::max(ns, 1);
+  p.tps = nKV == 0 ? 1 : (nKV + ns - 1) / ns;
+  p.NS = nKV == 0 ? 1 : (nKV + p.tps - 1) / p.tps;
+  return p;
+}
+
+size_t decode_workspace_bytes(int B, int Hkv, int Skv, int D) {
+  const DecodePlan p = decode_plan(B, Hkv, Skv);
+  if (p.NS == 1) return 0;
+  return (size_t)B * Hkv * p.NS * 32 * ((size_t)D + 2) * 4;
+}
+
+hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream) {
+  switch (score_mod) {
+    case SM_NONE: return launch_dec_mask<SM_NONE>(a, causal, stream);
+    case SM_ALIBI: return launch_dec_mask<SM_ALIBI>(a, causal, stream);
+    case SM_SOFTCAP:
+      return a.fixed_ref ? launch_dec_mask<SM_SOFTCAP_FIXED>(a, causal, stream)
+                         : launch_dec_mask<SM_SOFTCAP>(a, causal, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace av

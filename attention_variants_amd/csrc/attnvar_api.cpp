@@ -100,6 +100,65 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   return hip_status(av::launch_attn_fwd(a, D, var->score_mod, var->mask, stream));
 }
 
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv < 0 || D <= 0) return 0;
+  return av::decode_workspace_bytes(B, Hkv, Skv, D);
+}
+
+int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                    hipStream_t stream) {
+  if (var == nullptr) return AV_ERR_NULL;
+  if ((Sq > 0 && (q == nullptr || out == nullptr)) || (Skv > 0 && (k == nullptr || v == nullptr)))
+    return AV_ERR_NULL;
+  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
+  if (var->mask != AV_MASK_NONE && var->mask != AV_MASK_CAUSAL) return AV_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return AV_ERR_SHAPE;
+  if (var->kv_group != 0 && var->kv_group != Hq / Hkv) return AV_ERR_SHAPE;
+  if (var->mask == AV_MASK_CAUSAL && Skv < Sq) return AV_ERR_SHAPE;
+  if (D != 64) return AV_ERR_UNSUPPORTED;
+  if ((int64_t)(Hq / Hkv) * Sq > 32) return AV_ERR_UNSUPPORTED;
+  if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
+  if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
+  if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  if (Sq == 0) return AV_OK;
+  const av::DecodePlan plan = av::decode_plan(B, Hkv, Skv);
+  const int64_t total = (int64_t)B * Hkv * plan.NS;
+  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
+  const size_t need = av::decode_workspace_bytes(B, Hkv, Skv, D);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return AV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return AV_ERR_ALIGN;
+
+  av::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.ws_o = need > 0 ? (float*)workspace : nullptr;
+  a.ws_ml = need > 0 ? (float*)workspace + (size_t)B * Hkv * plan.NS * 32 * D : nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.g = Hq / Hkv;
+  a.NS = plan.NS;
+  a.tps = plan.tps;
+  a.total = (int)total;
+  const double scale = var->scale > 0.f ? (double)var->scale : 1.0 / sqrt((double)D);
+  a.scale = (float)scale;
+  a.c = (float)(scale * kLog2e);
+  a.alibi_max_bias = var->alibi_max_bias;
+  a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
+  a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
+  return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
+}
+
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,
                   float lambda, float scale, int causal, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;

@@ -58,6 +58,31 @@ hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hi
 // (SM_BIAS) or column-wise (SM_GATE).
 hipError_t launch_evo_attention(const AttnArgs& a, int col, hipStream_t stream);
 
+// Decoding / short-query attention (split-KV): the Sq queries are the last
+// Sq positions of the keys; one workgroup per (batch, KV head, key split)
+// holds the g*Sq <= 32 query rows of the KV head's query heads.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;        // nullable
+  float* ws_o;       // [B*Hkv, NS, 32, D] partial O of each split (NS > 1)
+  float* ws_ml;      // [B*Hkv, NS, 32, 2] (max, sum) of each split
+  int B, Hq, Hkv, Sq, Skv;
+  int g;             // Hq / Hkv
+  int NS, tps;       // key splits, 64-key tiles per split
+  int total;         // B * Hkv * NS
+  float c, scale, alibi_max_bias, softcap;
+  int fixed_ref;
+};
+struct DecodePlan {
+  int NS, tps;
+};
+DecodePlan decode_plan(int B, int Hkv, int Skv);
+size_t decode_workspace_bytes(int B, int Hkv, int Skv, int D);
+hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream);
+
 struct DiffArgs {
   const void* q;
   const void* k;

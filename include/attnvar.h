@@ -104,6 +104,24 @@ typedef struct {
 int attn_fwd(const av_variant* variant, const void* q, const void* k, const void* v, void* out,
              float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream);
 
+/* Decoding / short-query attention forward (split over the keys).  The
+ * pages' serving workload decodes causal and softcapped LLaMA-3.2-1B variants
+ * under vLLM (talk notes, end-to-end section); the operation is attn_fwd's,
+ * with the queries placed at the end of the keys: query q of a sequence has
+ * absolute position Skv - Sq + q, which the causal mask and the ALiBi
+ * distance use.
+ *   q [B, Hq, Sq, D]   k, v [B, Hkv, Skv, D]   out [B, Hq, Sq, D]
+ *   lse [B, Hq, Sq] fp32, nullable (natural log, as attn_fwd)
+ * Supported: D = 64; (Hq/Hkv) * Sq <= 32 (all queries of one KV head fit one
+ * 32-row block); mask none or causal (causal needs Skv >= Sq); every score
+ * modifier.  `workspace` (device, caller-owned, 16-byte aligned) must hold
+ * attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) bytes; when that is 0
+ * it may be NULL.  Skv == 0 writes zero rows and lse = -inf. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
+int attn_decode_fwd(const av_variant* variant, const void* q, const void* k, const void* v, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                    hipStream_t stream);
+
 /* Differential attention forward (talk notes, "Background and motivation"
  * and "Evaluation: complex attention variants"; the pages name the variant
  * without a formula; the reading implemented is):

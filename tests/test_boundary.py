@@ -136,6 +136,32 @@ def test_evoformer_rejections(lib):
     assert call(ws=0x100000 + 16) == -4
 
 
+def test_decode_rejections(lib):
+    assert lib.attn_decode_workspace_bytes(1, 32, 8, 1, 4096, 64) > 0     # few KV heads: keys split
+    assert lib.attn_decode_workspace_bytes(128, 32, 8, 1, 4096, 64) == 0  # enough workgroups: one split
+    assert lib.attn_decode_workspace_bytes(0, 32, 8, 1, 4096, 64) == 0
+
+    def call(score_mod=0, mask=1, q=P, k=P2, v=P3, out=P4, lse=None, ws=0x200000, wsb=1 << 30, B=1, Hq=32,
+             Hkv=8, Sq=1, Skv=4096, D=64, scale=0.0):
+        var = av.AvVariant(score_mod, mask, scale, 20.0, 8.0, 256, 0, None, 0)
+        return lib.attn_decode_fwd(ctypes.byref(var), q, k, v, out, lse, ws, wsb, B, Hq, Hkv, Sq, Skv, D, None)
+
+    assert call(q=None) == -1
+    assert call(k=None) == -1
+    assert call(mask=2) == -3          # only none and causal
+    assert call(score_mod=7) == -3
+    assert call(Hq=30) == -2           # Hq not a multiple of Hkv
+    assert call(Skv=0, Sq=1) == -2     # causal queries must lie inside the keys
+    assert call(D=128) == -3
+    assert call(Sq=9) == -3            # 4 heads x 9 queries > 32 rows
+    assert call(scale=float("nan")) == -7
+    assert call(out=P4 + 2) == -4
+    assert call(ws=None) == -5         # B=1: the keys are split, a workspace is needed
+    assert call(wsb=16) == -5
+    assert call(ws=0x200000 + 8) == -4
+    assert call(Sq=0) == 0
+
+
 def test_evoformer_column_rejections(lib):
     def call(m=P, w=P2, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):
         if wsb is None:
