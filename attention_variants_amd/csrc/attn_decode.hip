@@ -22,7 +22,7 @@
 //  * At the end the 4 waves merge (m, l, O) through LDS.  With one split the
 //    result is final; with several, each split writes its partial state to
 //    the workspace and a second kernel merges the splits (the same rescale as
-//    the online softmax).
+//    the online softmax), one workgroup per output row.
 
 #include <algorithm>
 
@@ -35,6 +35,14 @@ namespace {
 constexpr int NT = 256;
 constexpr int BN = 64;   // keys per tile
 constexpr int ROWS = 32; // query rows per workgroup (one MFMA block)
+#ifndef AV_DECODE_TARGET_WG
+#define AV_DECODE_TARGET_WG 512
+#endif
+#ifndef AV_DECODE_MIN_TILES
+#define AV_DECODE_MIN_TILES 4
+#endif
+constexpr int kDecodeTargetWG = AV_DECODE_TARGET_WG;
+constexpr int kDecodeMinTiles = AV_DECODE_MIN_TILES;
 
 template <int D, int SM, bool CAUSAL>
 __global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) {
@@ -236,39 +244,48 @@ __global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) 
   }
 }
 
-// Merge of the key splits: one thread per (row, 4 columns).
+// Merge of the key splits: one workgroup per output row (batch, KV head,
+// packed row); lane = column (D = 64), the 4 waves take the splits
+// round-robin and meet in LDS.
 template <int D>
 __global__ __launch_bounds__(NT) void attn_decode_combine(const DecodeArgs a) {
+  static_assert(D == 64, "one lane per column");
+  __shared__ float red[4][D + 2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = a.g * a.Sq;
-  const long long n = (long long)a.B * a.Hkv * R * (D / 4);
-  const long long i = (long long)blockIdx.x * NT + threadIdx.x;
-  if (i >= n) return;
-  const int d4 = (int)(i % (D / 4));
-  const long long rowi = i / (D / 4);
-  const int rr = (int)(rowi % R);
-  const int bk = (int)(rowi / R);
+  const int rr = blockIdx.x % R;
+  const int bk = blockIdx.x / R;
+  const float* ml = a.ws_ml + ((size_t)bk * a.NS * ROWS + rr) * 2;  // split s at ml[s * ROWS * 2]
+  const float* os = a.ws_o + ((size_t)bk * a.NS * ROWS + rr) * D;   // split s at os[s * ROWS * D]
+  // pass 1: the common reference M = max over the splits
   float M = neg_inf();
-  for (int s = 0; s < a.NS; ++s) M = fmaxf(M, a.ws_ml[(((size_t)bk * a.NS + s) * ROWS + rr) * 2]);
+  for (int s = tid; s < a.NS; s += NT) M = fmaxf(M, ml[(size_t)s * ROWS * 2]);
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[w][0] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
   const float Msub = M == neg_inf() ? 0.f : M;
-  float Lsum = 0.f;
-  f32x4 acc = {};
-  for (int s = 0; s < a.NS; ++s) {
-    const size_t unit = ((size_t)bk * a.NS + s) * ROWS + rr;
-    const float f = exp2_fast(a.ws_ml[unit * 2] - Msub);
-    Lsum = fmaf(a.ws_ml[unit * 2 + 1], f, Lsum);
-    const f32x4 x = *(const f32x4*)(a.ws_o + unit * D + d4 * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = fmaf(x[e], f, acc[e]);
+  __syncthreads();
+  // pass 2: rescaled sums of this wave's splits
+  float acc = 0.f, lsum = 0.f;
+#pragma unroll 4
+  for (int s = w; s < a.NS; s += 4) {
+    const float f = exp2_fast(ml[(size_t)s * ROWS * 2] - Msub);
+    lsum = fmaf(ml[(size_t)s * ROWS * 2 + 1], f, lsum);
+    acc = fmaf(os[(size_t)s * ROWS * D + lane], f, acc);
   }
+  red[w][lane] = acc;
+  if (lane == 0) red[w][D] = lsum;
+  __syncthreads();
+  if (w != 0) return;
+  const float L = red[0][D] + red[1][D] + red[2][D] + red[3][D];
+  const float x = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   const int hk = bk % a.Hkv, b = bk / a.Hkv;
   const int ohq = hk * a.g + rr / a.Sq, oq = rr % a.Sq;
   const size_t orow = ((size_t)b * a.Hq + ohq) * a.Sq + oq;
-  const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  bf16x4 val;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) val[e] = (bf16)(acc[e] * inv);
-  *(bf16x4*)((bf16*)a.o + orow * D + d4 * 4) = val;
-  if (a.lse != nullptr && d4 == 0) a.lse[orow] = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : neg_inf();
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  ((bf16*)a.o)[orow * D + lane] = (bf16)(x * inv);
+  if (a.lse != nullptr && lane == 0) a.lse[orow] = L > 0.f ? (M + __log2f(L)) * kLn2 : neg_inf();
 }
 
 template <int D, int SM, bool CAUSAL>
@@ -276,8 +293,8 @@ hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_decode_kernel<D, SM, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.NS == 1) return e;
-  const long long n = (long long)a.B * a.Hkv * a.g * a.Sq * (D / 4);
-  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)((n + NT - 1) / NT)), dim3(NT), 0, stream, a);
+  const long long rows = (long long)a.B * a.Hkv * a.g * a.Sq;
+  hipLaunchKernelGGL((attn_decode_combine<D>), dim3((unsigned)rows), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -292,10 +309,10 @@ DecodePlan decode_plan(int B, int Hkv, int Skv) {
   DecodePlan p{};
   const int nKV = (Skv + 63) / 64;
   const int units = B * Hkv;
-  // enough workgroups to fill the chip (3 per CU), and at least 4 tiles
-  // (one per wave) in every split
-  int ns = (768 + units - 1) / units;
-  ns = std::min(ns, std::max(1, nKV / 4));
+  // enough workgroups to fill the chip (kDecodeTargetWG), and at least
+  // kDecodeMinTiles 64-key tiles in every split
+  int ns = (kDecodeTargetWG + units - 1) / units;
+  ns = std::min(ns, std::max(1, nKV / kDecodeMinTiles));
   ns = std::max(ns, 1);
   p.tps = nKV == 0 ? 1 : (nKV + ns - 1) / ns;
   p.NS = nKV == 0 ? 1 : (nKV + p.tps - 1) / p.tps;

@@ -128,7 +128,7 @@ int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const v
   if (Sq == 0) return AV_OK;
   const av::DecodePlan plan = av::decode_plan(B, Hkv, Skv);
   const int64_t total = (int64_t)B * Hkv * plan.NS;
-  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
+  if (total > INT32_MAX || (int64_t)B * Hkv * 32 > INT32_MAX) return AV_ERR_TOO_LARGE;
   const size_t need = av::decode_workspace_bytes(B, Hkv, Skv, D);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return AV_ERR_WORKSPACE;
   if (need > 0 && !aligned(workspace, 16)) return AV_ERR_ALIGN;

@@ -295,6 +295,21 @@ def run_sweep(path, steps, warmup):
         emit({"kernel": "diff_attn_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "executed_tflops": round(tf * 1.5, 1),
               "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+    # decoding: one new query per sequence against its key/value cache
+    # (LLaMA-3.2-1B attention shape: 32 query heads, 8 KV heads, D = 64)
+    for (B, Skv) in ((64, 4096), (8, 16384), (1, 16384)):
+        Hq, Hkv, D = 32, 8, 64
+        x = wi.attention_inputs(B, Hq, Hkv, 1, Skv, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, av.attn_decode_workspace_bytes(B, Hq, Hkv, 1, Skv, D)), dtype=torch.uint8, device=dev)
+        for sm, mk in (("none", "causal"), ("softcap", "causal")):
+            _, per = time_launches([lambda: av.attn_decode_fwd(q, k, v, score_mod=sm, mask=mk, out=out,
+                                                                workspace=ws)], steps, warmup)
+            byts = 2 * (2 * B * Hkv * Skv * D + 2 * B * Hq * D)
+            emit({"kernel": "attn_decode_fwd", "score_mod": sm, "mask": mk, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": 1,
+                  "Skv": Skv, "D": D, "us": round(per[0] * 1e3, 2), "hbm_gbs": round(byts / (per[0] * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(byts / (per[0] * 1e-3) / 8e12, 4)})
     for Nr in (256, 384, 768):
         Ns, Cm, Hh, dh = 128, 256, 8, 32
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
@@ -367,6 +382,18 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "evoformer_col", "Ns": Ns, "Nr": Nr, "launches": steps}))
         return
+    if what == "decode":
+        B, Hq, Hkv, Skv, D = 64, 32, 8, 4096, 64
+        x = wi.attention_inputs(B, Hq, Hkv, 1, Skv, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, av.attn_decode_workspace_bytes(B, Hq, Hkv, 1, Skv, D)), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.attn_decode_fwd(q, k, v, score_mod="softcap", mask="causal", out=out, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "decode", "B": B, "Hq": Hq, "Hkv": Hkv, "Skv": Skv, "launches": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -398,7 +425,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
-    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff"],
+    ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
+                                          "decode"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")

@@ -138,7 +138,7 @@ def test_evoformer_rejections(lib):
 
 def test_decode_rejections(lib):
     assert lib.attn_decode_workspace_bytes(1, 32, 8, 1, 4096, 64) > 0     # few KV heads: keys split
-    assert lib.attn_decode_workspace_bytes(128, 32, 8, 1, 4096, 64) == 0  # enough workgroups: one split
+    assert lib.attn_decode_workspace_bytes(64, 32, 8, 1, 4096, 64) == 0   # enough workgroups: one split
     assert lib.attn_decode_workspace_bytes(0, 32, 8, 1, 4096, 64) == 0
 
     def call(score_mod=0, mask=1, q=P, k=P2, v=P3, out=P4, lse=None, ws=0x200000, wsb=1 << 30, B=1, Hq=32,
