@@ -77,8 +77,18 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   constexpr int KP = D + 8;          // K row pitch (elements): 16 rows hit 16 distinct 16-byte bank slots
   static_assert(NCH >= 1 && BN * CPR % NT == 0, "tile/thread mismatch");
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];  // swizzled for transposed reads
+  // LDS: the K/V double buffer during the key loop; before it the Q tile
+  // and after it the O tile pass through the same bytes, so that Q is read
+  // and O written as whole contiguous rows (row pitch KP).
+  // (Q/O staging: all but the gated Evoformer forms and the document mask,
+  // whose short rows or register budget gain nothing from it)
+  constexpr bool kStageQO = SM != SM_BIAS && SM != SM_GATE && MK != MK_DOC;
+  constexpr int KV_BYTES = 2 * BN * KP * 2 + 2 * BN * D * 2;
+  constexpr int QO_BYTES = BM * KP * 2;
+  __shared__ __attribute__((aligned(16))) char lds_raw[(kStageQO && QO_BYTES > KV_BYTES) ? QO_BYTES : KV_BYTES];
+  bf16 (*Ks)[BN * KP] = reinterpret_cast<bf16 (*)[BN * KP]>(lds_raw);
+  bf16 (*Vs)[BN * D] = reinterpret_cast<bf16 (*)[BN * D]>(lds_raw + 2 * BN * KP * 2);  // swizzled for transposed reads
+  bf16* QOs = reinterpret_cast<bf16*>(lds_raw);
   __shared__ __attribute__((aligned(16))) int Ds[2][MK == MK_DOC ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -135,12 +145,37 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   }
 
   // ---- Q^T operands in registers: lane holds query qi[qb], 8 consecutive d per k-step
+  // rows q0 .. q0+BM-1 of this (b, hq) slice are contiguous: 16-byte chunks,
+  // consecutive threads on consecutive chunks, through LDS into the operands
+  constexpr int QCH = BM * CPR / NT;  // Q chunks per thread
+  static_assert(BM * CPR % NT == 0, "Q tile/thread mismatch");
   bf16x8 qreg[QB][NDS];
+  if constexpr (!kStageQO) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      qreg[qb][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(qi[qb] * D + s * 16 + hh * 8) * 2));
+      for (int s = 0; s < NDS; ++s)
+        qreg[qb][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(qi[qb] * D + s * 16 + hh * 8) * 2));
+  } else {
+    i32x4 qst[QCH];
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+      const int idx = tid + NT * c;
+      qst[c] = buf_load16(qrs, (uint32_t)((q0 + idx / CPR) * D + (idx % CPR) * 8) * 2);
+    }
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+      const int idx = tid + NT * c;
+      *(i32x4*)&QOs[(idx / CPR) * KP + (idx % CPR) * 8] = qst[c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
+        qreg[qb][s] = *(const bf16x8*)&QOs[(qi[qb] - q0) * KP + s * 16 + hh * 8];
+    __syncthreads();  // the key loop reuses these bytes
+  }
 
   f32x16 o[QB][NDB];
 #pragma unroll
@@ -457,7 +492,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     tile(__builtin_amdgcn_readfirstlane((int)full) != 0, buf, n0);
   }
 
-  // ---- epilogue: O / l, bf16 store, optional LSE
+  // ---- epilogue: O / l, bf16 store (staged through LDS), optional LSE
+  if constexpr (kStageQO) __syncthreads();  // every wave is done with the K/V tiles
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = xhalf_sum(st[qb].l);
@@ -486,7 +522,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         }
       }
     } else {
-      bf16* orow = (bf16*)a.o + qoff + (size_t)q * D;
+      bf16* orow = kStageQO ? QOs + (q - q0) * KP : (bf16*)a.o + qoff + (size_t)q * D;  // staged: written out below
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -501,6 +537,17 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         a.lse[((size_t)b * a.Hq + hq) * a.Sq + q] =
             l_tot > 0.f ? (st[qb].m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
       }
+    }
+  }
+  if constexpr (kStageQO) {
+    // O tile: rows q0 .. q0+BM-1 of the (b, hq) slice, contiguous in memory
+    __syncthreads();
+    bf16* obase = (bf16*)a.o + qoff;
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+      const int idx = tid + NT * c;
+      const int row = idx / CPR, col = idx % CPR;
+      if (q0 + row < a.Sq) *(i32x4*)(obase + (size_t)(q0 + row) * D + col * 8) = *(const i32x4*)&QOs[row * KP + col * 8];
     }
   }
 }
