@@ -193,6 +193,39 @@ def attention(
     return out, lse
 
 
+def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, *, page_size: int,
+                           score_mod: str = "none", mask: str = "none", scale: float | None = None,
+                           softcap: float = 20.0, alibi_max_bias: float = 8.0):
+    """Decoding against a paged key/value cache.
+
+    The pages' serving workload runs under vLLM (talk notes, end-to-end
+    section), whose key/value cache is paged.  Reading: sequence b holds
+    seq_lens[b] keys; key j lives in page block_table[b, j // page_size], slot
+    j % page_size, of a cache laid out [num_pages, Hkv, page_size, D]; its Sq
+    queries are its last Sq positions.  Gather each sequence's keys, then the
+    plain definition (``attention`` with q_offset = seq_lens[b] - Sq).
+
+    q [B, Hq, Sq, D] -> (out [B, Hq, Sq, D], lse [B, Hq, Sq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    block_table = np.asarray(block_table)
+    B, Hq, Sq, D = q.shape
+    out = np.zeros((B, Hq, Sq, vc.shape[-1]))
+    lse = np.zeros((B, Hq, Sq))
+    for b in range(B):
+        n = int(seq_lens[b])
+        j = np.arange(n)
+        pages = block_table[b, j // page_size]
+        kb = kc[pages, :, j % page_size].transpose(1, 0, 2)[None]  # [1, Hkv, n, D]
+        vb = vc[pages, :, j % page_size].transpose(1, 0, 2)[None]
+        o, l_ = attention(q[b:b + 1], kb, vb, score_mod=score_mod, mask=mask, scale=scale, softcap=softcap,
+                          alibi_max_bias=alibi_max_bias, q_offset=n - Sq)
+        out[b], lse[b] = o[0], l_[0]
+    return out, lse
+
+
 # --------------------------------------------------------------------------
 # Differential attention.  The pages name it among the variants that
 # templates cannot express (talk notes, "Background and motivation" and

@@ -482,6 +482,47 @@ def test_decode_queries_at_the_end(score_mod):
         oracle.attention(q[:, :, :3], k, v, mask="causal", q_offset=0)
 
 
+def test_paged_decode_pins():
+    """A paged cache equals the dense cache it stores; shuffling the pages
+    (with the block table) changes nothing; each sequence only sees its own
+    length."""
+    B, Hq, Hkv, Sq, D, ps = 3, 4, 2, 2, 8, 4
+    lens = [9, 2, 12]
+    maxp = 3
+    rng = np.random.default_rng(60)
+    dense_k = [_rand((1, Hkv, n, D), 61 + b) for b, n in enumerate(lens)]
+    dense_v = [_rand((1, Hkv, n, D), 71 + b) for b, n in enumerate(lens)]
+    q = _rand((B, Hq, Sq, D), 80)
+    npages = B * maxp
+    perm = rng.permutation(npages)
+    kc = np.zeros((npages, Hkv, ps, D))
+    vc = np.zeros((npages, Hkv, ps, D))
+    bt = np.zeros((B, maxp), dtype=np.int32)
+    for b, n in enumerate(lens):
+        for p in range(maxp):
+            bt[b, p] = perm[b * maxp + p]
+            for s in range(ps):
+                j = p * ps + s
+                if j < n:
+                    kc[bt[b, p], :, s] = dense_k[b][0, :, j]
+                    vc[bt[b, p], :, s] = dense_v[b][0, :, j]
+    for mask in ("none", "causal"):
+        out, lse = oracle.paged_decode_attention(q, kc, vc, bt, lens, page_size=ps, score_mod="softcap", mask=mask)
+        for b, n in enumerate(lens):
+            ref, ref_lse = oracle.attention(q[b:b + 1], dense_k[b], dense_v[b], score_mod="softcap", mask=mask,
+                                            q_offset=n - Sq)
+            np.testing.assert_allclose(out[b:b + 1], ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[b:b + 1], ref_lse, rtol=0, atol=1e-12)
+    # relabel the pages once more: same result
+    perm2 = rng.permutation(npages)
+    inv = np.empty_like(perm2)
+    inv[perm2] = np.arange(npages)
+    out2, _ = oracle.paged_decode_attention(q, kc[perm2], vc[perm2], inv[bt], lens, page_size=ps, mask="causal",
+                                            score_mod="softcap")
+    out1, _ = oracle.paged_decode_attention(q, kc, vc, bt, lens, page_size=ps, mask="causal", score_mod="softcap")
+    np.testing.assert_allclose(out2, out1, rtol=0, atol=1e-12)
+
+
 def _evo_ungated(m, wq, wk, wv, bias, H, dh):
     """Independent loop form: per sequence, head and row."""
     Ns, Nr, _ = m.shape
