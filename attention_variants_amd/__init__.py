@@ -36,6 +36,8 @@ EXPORTED = (
     "attn_fwd",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
+    "attn_decode_paged_workspace_bytes",
+    "attn_decode_paged_fwd",
     "diff_attn_fwd",
     "evoformer_workspace_bytes",
     "evoformer_gated_attn_fwd",
@@ -84,6 +86,11 @@ def load_library(path: str | None = None):
     lib.attn_decode_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                     _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_decode_fwd.restype = _i
+    lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
+    lib.attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_decode_paged_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                          ctypes.c_size_t, _i, _i, _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_decode_paged_fwd.restype = _i
     lib.diff_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp]
     lib.diff_attn_fwd.restype = _i
     lib.evoformer_workspace_bytes.argtypes = [_i, _i, _i, _i]
@@ -213,6 +220,49 @@ def attn_decode_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softca
                              0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, Skv, D,
                              _stream_ptr(q.device))
     _check(rc, "attn_decode_fwd")
+    return (out, lse) if return_lse else out
+
+
+def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_mod="none", mask="none", scale=0.0,
+                          softcap=20.0, alibi_max_bias=8.0, kv_group=0, return_lse=False, out=None, lse=None,
+                          workspace=None):
+    """Decoding against a paged cache: k_cache/v_cache [num_pages, Hkv, page_size, D] bf16,
+    block_table [B, max_pages] int32, seq_lens [B] int32; q [B, Hq, Sq, D] are the last Sq
+    positions of each sequence -> out [B, Hq, Sq, D].
+    """
+    import torch
+
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    _need(k_cache, "k_cache", torch.bfloat16, 4)
+    _need(v_cache, "v_cache", torch.bfloat16, 4)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    B, Hq, Sq, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache / v_cache must be [num_pages, Hkv, page_size, D]")
+    if block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    max_pages = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 4)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    need = lib.attn_decode_paged_workspace_bytes(B, Hq, Hkv, Sq, D, page_size, max_pages) if Sq > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
+                       kv_group=kv_group)
+    rc = lib.attn_decode_paged_fwd(ctypes.byref(var), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                   None if lse is None else lse.data_ptr(),
+                                   None if workspace is None else workspace.data_ptr(),
+                                   0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, D, page_size,
+                                   max_pages, num_pages, _stream_ptr(q.device))
+    _check(rc, "attn_decode_paged_fwd")
     return (out, lse) if return_lse else out
 
 

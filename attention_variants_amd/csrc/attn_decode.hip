@@ -44,8 +44,9 @@ constexpr int ROWS = 32; // query rows per workgroup (one MFMA block)
 constexpr int kDecodeTargetWG = AV_DECODE_TARGET_WG;
 constexpr int kDecodeMinTiles = AV_DECODE_MIN_TILES;
 
-template <int D, int SM, bool CAUSAL>
-__global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) {
+// (the paged form holds 64-bit row addresses: two waves per SIMD instead of three)
+template <int D, int SM, bool CAUSAL, bool PAGED>
+__global__ __launch_bounds__(NT, (PAGED ? 2 : 3)) void attn_decode_kernel(const DecodeArgs a) {
   constexpr int NKB = BN / 32, NDB = D / 32, NDS = D / 16, NPS = BN / 16;
   constexpr int VCH = BN * D / 8 / 64;  // 16-byte V chunks per lane per tile
   __shared__ __attribute__((aligned(16))) bf16 Vs[4][BN * D];  // one slot per wave, swizzled
@@ -64,18 +65,44 @@ __global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) 
   const bool row_live = r < R;
   const int hq = hk * a.g + (row_live ? r / a.Sq : 0);
   const int qq = row_live ? r % a.Sq : 0;
-  const int pos = a.Skv - a.Sq + qq;  // absolute position of the query
+  // key count of this sequence (paged: its own length, at most the table's reach)
+  const int Skv = PAGED ? min(max(a.seq_lens[b], 0), a.max_pages * a.page_size) : a.Skv;
+  const int pos = Skv - a.Sq + qq;  // absolute position of the query
   const auto qrs = make_rsrc((const bf16*)a.q + (((size_t)b * a.Hq + hq) * a.Sq + qq) * D,
                              row_live ? (uint32_t)D * 2 : 0u);
   bf16x8 qreg[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(s * 16 + hh * 8) * 2));
 
-  const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
-  const auto krs = make_rsrc((const bf16*)a.k + kvoff, (uint32_t)a.Skv * D * 2);
-  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, (uint32_t)a.Skv * D * 2);
+  const size_t kvoff = PAGED ? 0 : ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
+  const auto krs = make_rsrc((const bf16*)a.k + kvoff, PAGED ? 0u : (uint32_t)a.Skv * D * 2);
+  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, PAGED ? 0u : (uint32_t)a.Skv * D * 2);
+  // Paged cache [num_pages, Hkv, page_size, D]: the pages of one 64-key tile
+  // (64 / page_size of them) are looked up once per tile, lane i holding the
+  // tile's i-th page; rows past the sequence reuse its last page (masked) and
+  // page ids are clamped into the cache, so a bad table cannot fault.
+  const int* bt_row = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+  const int last_pidx = PAGED ? max(Skv - 1, 0) / a.page_size : 0;
+  auto tile_page = [&](int n0) {
+    if constexpr (PAGED) {
+      const int np = BN / a.page_size;
+      const int pidx = min(n0 / a.page_size + lane % np, last_pidx);
+      return min(max(bt_row[pidx], 0), a.num_pages - 1);
+    } else {
+      return 0;
+    }
+  };
+  // element offset of key row n0 + row (paged: via the tile's page ids)
+  auto key_off = [&](int pg, int n0, int row) -> size_t {
+    if constexpr (PAGED) {
+      const int page = __shfl(pg, row / a.page_size);
+      return (((size_t)page * a.Hkv + hk) * a.page_size + row % a.page_size) * D;
+    } else {
+      return (size_t)(n0 + row) * D;
+    }
+  };
 
-  const int nKV = (a.Skv + BN - 1) / BN;
+  const int nKV = (Skv + BN - 1) / BN;
   const int t_lo = split * a.tps, t_hi = min(nKV, t_lo + a.tps);
 
   f32x16 o[NDB];
@@ -94,21 +121,33 @@ __global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) 
 
   for (int t = t_lo + w; t < t_hi; t += 4) {
     const int n0 = t * BN;
+    const int pg = tile_page(n0);
     // ---- V tile -> registers -> this wave's LDS slot (row-major, swizzled)
     i32x4 vr[VCH];
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = lane + 64 * c;
       const int row = idx / (D / 8), col = idx % (D / 8);
-      vr[c] = buf_load16(vrs, (uint32_t)((n0 + row) * D + col * 8) * 2);
+      if constexpr (PAGED) {
+        vr[c] = *(const i32x4*)((const bf16*)a.v + key_off(pg, n0, row) + col * 8);
+      } else {
+        vr[c] = buf_load16(vrs, (uint32_t)((n0 + row) * D + col * 8) * 2);
+      }
     }
     // ---- K fragments straight into the A operand: key kb*32 + l32, d = st*16 + 8*hh .. +7
     bf16x8 kf[NKB][NDS];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      const size_t koff = key_off(pg, n0, kb * 32 + l32);
 #pragma unroll
-      for (int s = 0; s < NDS; ++s)
-        kf[kb][s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (uint32_t)((n0 + kb * 32 + l32) * D + s * 16 + hh * 8) * 2));
+      for (int s = 0; s < NDS; ++s) {
+        if constexpr (PAGED) {
+          kf[kb][s] = *(const bf16x8*)((const bf16*)a.k + koff + s * 16 + hh * 8);
+        } else {
+          kf[kb][s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (uint32_t)((n0 + kb * 32 + l32) * D + s * 16 + hh * 8) * 2));
+        }
+      }
+    }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = lane + 64 * c;
@@ -139,9 +178,9 @@ __global__ __launch_bounds__(NT, 3) void attn_decode_kernel(const DecodeArgs a) 
         }
       }
     // ---- mask: keys past the end, and (causal) keys after the query's position
-    const bool full = (n0 + BN <= a.Skv) && (!CAUSAL || n0 + BN - 1 <= a.Skv - a.Sq);
+    const bool full = (n0 + BN <= Skv) && (!CAUSAL || n0 + BN - 1 <= Skv - a.Sq);
     if (!full) {
-      int lim = a.Skv - kbase, rel = pos - kbase;
+      int lim = Skv - kbase, rel = pos - kbase;
       asm volatile("" : "+v"(lim), "+v"(rel));
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -290,7 +329,11 @@ __global__ __launch_bounds__(NT) void attn_decode_combine(const DecodeArgs a) {
 
 template <int D, int SM, bool CAUSAL>
 hipError_t launch_dec(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_decode_kernel<D, SM, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+  if (a.block_table != nullptr) {
+    hipLaunchKernelGGL((attn_decode_kernel<D, SM, CAUSAL, true>), dim3(a.total), dim3(NT), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_decode_kernel<D, SM, CAUSAL, false>), dim3(a.total), dim3(NT), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.NS == 1) return e;
   const long long rows = (long long)a.B * a.Hkv * a.g * a.Sq;

@@ -159,6 +159,75 @@ int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const v
   return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
 }
 
+size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Sq, int D, int page_size, int max_pages) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || D <= 0 || page_size <= 0 || max_pages <= 0) return 0;
+  if ((int64_t)max_pages * page_size > INT32_MAX - 64) return 0;
+  return av::decode_workspace_bytes(B, Hkv, max_pages * page_size, D);
+}
+
+int attn_decode_paged_fwd(const av_variant* var, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int D,
+                          int page_size, int max_pages, int num_pages, hipStream_t stream) {
+  if (var == nullptr) return AV_ERR_NULL;
+  if (Sq > 0 && (q == nullptr || out == nullptr || k_cache == nullptr || v_cache == nullptr ||
+                 block_table == nullptr || seq_lens == nullptr))
+    return AV_ERR_NULL;
+  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
+  if (var->mask != AV_MASK_NONE && var->mask != AV_MASK_CAUSAL) return AV_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || D <= 0 || max_pages <= 0 || num_pages <= 0) return AV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return AV_ERR_SHAPE;
+  if (var->kv_group != 0 && var->kv_group != Hq / Hkv) return AV_ERR_SHAPE;
+  if (page_size != 16 && page_size != 32 && page_size != 64) return AV_ERR_UNSUPPORTED;
+  if (D != 64) return AV_ERR_UNSUPPORTED;
+  if ((int64_t)(Hq / Hkv) * Sq > 32) return AV_ERR_UNSUPPORTED;
+  if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
+  if (!aligned(block_table, 4) || !aligned(seq_lens, 4)) return AV_ERR_ALIGN;
+  if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
+  if ((int64_t)max_pages * page_size > INT32_MAX - 64) return AV_ERR_TOO_LARGE;
+  if (Sq == 0) return AV_OK;
+  const int Skv_max = max_pages * page_size;
+  const av::DecodePlan plan = av::decode_plan(B, Hkv, Skv_max);
+  const int64_t total = (int64_t)B * Hkv * plan.NS;
+  if (total > INT32_MAX || (int64_t)B * Hkv * 32 > INT32_MAX) return AV_ERR_TOO_LARGE;
+  const size_t need = av::decode_workspace_bytes(B, Hkv, Skv_max, D);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return AV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return AV_ERR_ALIGN;
+
+  av::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = out;
+  a.lse = lse;
+  a.ws_o = need > 0 ? (float*)workspace : nullptr;
+  a.ws_ml = need > 0 ? (float*)workspace + (size_t)B * Hkv * plan.NS * 32 * D : nullptr;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv_max;
+  a.g = Hq / Hkv;
+  a.NS = plan.NS;
+  a.tps = plan.tps;
+  a.total = (int)total;
+  const double scale = var->scale > 0.f ? (double)var->scale : 1.0 / sqrt((double)D);
+  a.scale = (float)scale;
+  a.c = (float)(scale * kLog2e);
+  a.alibi_max_bias = var->alibi_max_bias;
+  a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
+  a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.page_size = page_size;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
+}
+
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,
                   float lambda, float scale, int causal, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;

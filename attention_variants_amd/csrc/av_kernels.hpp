@@ -75,6 +75,11 @@ struct DecodeArgs {
   int total;         // B * Hkv * NS
   float c, scale, alibi_max_bias, softcap;
   int fixed_ref;
+  // paged cache (block_table != nullptr): k, v are [num_pages, Hkv, page_size, D];
+  // Skv is then max_pages * page_size, the plan's bound on every sequence
+  const int* block_table;  // [B, max_pages]
+  const int* seq_lens;     // [B]
+  int page_size, max_pages, num_pages;
 };
 struct DecodePlan {
   int NS, tps;

@@ -122,6 +122,26 @@ int attn_decode_fwd(const av_variant* variant, const void* q, const void* k, con
                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                     hipStream_t stream);
 
+/* Decoding against a paged key/value cache (the vLLM-style serving layout of
+ * the pages' end-to-end workload; same operation and limits as
+ * attn_decode_fwd, with per-sequence key counts):
+ *   k_cache, v_cache [num_pages, Hkv, page_size, D]
+ *   block_table [B, max_pages] int32: key j of sequence b is in page
+ *     block_table[b, j / page_size], slot j % page_size
+ *   seq_lens [B] int32: keys of sequence b (<= max_pages * page_size; the Sq
+ *     queries are its last Sq positions)
+ * Device data are not read on the host: seq_lens is clamped to
+ * [0, max_pages * page_size] and page ids to [0, num_pages) in the kernel, so
+ * a bad table gives wrong rows, never an out-of-bounds access.  A sequence
+ * shorter than Sq under the causal mask gets zero rows (lse = -inf) for its
+ * queries that precede every key.  Supported page_size: 16, 32, 64.
+ * `workspace` as attn_decode_fwd, sized by attn_decode_paged_workspace_bytes. */
+size_t attn_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int Sq, int D, int page_size, int max_pages);
+int attn_decode_paged_fwd(const av_variant* variant, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, const int32_t* seq_lens, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int D,
+                          int page_size, int max_pages, int num_pages, hipStream_t stream);
+
 /* Differential attention forward (talk notes, "Background and motivation"
  * and "Evaluation: complex attention variants"; the pages name the variant
  * without a formula; the reading implemented is):

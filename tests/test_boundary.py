@@ -162,6 +162,32 @@ def test_decode_rejections(lib):
     assert call(Sq=0) == 0
 
 
+def test_paged_decode_rejections(lib):
+    assert lib.attn_decode_paged_workspace_bytes(1, 32, 8, 1, 64, 16, 1024) > 0
+    assert lib.attn_decode_paged_workspace_bytes(1, 32, 8, 1, 64, 0, 1024) == 0
+
+    def call(score_mod=2, mask=1, q=P, k=P2, v=P3, bt=0x50000, sl=0x60000, out=P4, ws=0x200000, wsb=1 << 30, B=1,
+             Hq=32, Hkv=8, Sq=1, D=64, ps=16, maxp=64, npages=64):
+        var = av.AvVariant(score_mod, mask, 0.0, 20.0, 8.0, 256, 0, None, 0)
+        return lib.attn_decode_paged_fwd(ctypes.byref(var), q, k, v, bt, sl, out, None, ws, wsb, B, Hq, Hkv, Sq, D,
+                                         ps, maxp, npages, None)
+
+    assert call(bt=None) == -1
+    assert call(sl=None) == -1
+    assert call(k=None) == -1
+    assert call(mask=3) == -3
+    assert call(ps=8) == -3
+    assert call(ps=48) == -3
+    assert call(D=128) == -3
+    assert call(Sq=9) == -3
+    assert call(maxp=0) == -2
+    assert call(npages=0) == -2
+    assert call(bt=0x50000 + 2) == -4
+    assert call(k=P2 + 8) == -4
+    assert call(ws=None) == -5
+    assert call(Sq=0) == 0
+
+
 def test_evoformer_column_rejections(lib):
     def call(m=P, w=P2, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):
         if wsb is None:
