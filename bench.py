@@ -310,6 +310,25 @@ def run_sweep(path, steps, warmup):
             emit({"kernel": "attn_decode_fwd", "score_mod": sm, "mask": mk, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": 1,
                   "Skv": Skv, "D": D, "us": round(per[0] * 1e3, 2), "hbm_gbs": round(byts / (per[0] * 1e-3) / 1e9, 1),
                   "frac_hbm_peak": round(byts / (per[0] * 1e-3) / 8e12, 4)})
+    # the same against a paged cache (16-key pages handed out in a shuffled order)
+    for (B, Skv, ps) in ((64, 4096, 16), (8, 16384, 64)):
+        Hq, Hkv, D = 32, 8, 64
+        npg = B * Skv // ps
+        x = wi.attention_inputs(npg, Hkv, Hkv, ps, ps, D)
+        kc, vc = _dev(x["k"], dev), _dev(x["v"], dev)
+        q = _dev(wi.attention_inputs(B, Hq, Hkv, 1, 1, D)["q"], dev)
+        bt = torch.from_numpy(np.random.default_rng(0).permutation(npg).astype(np.int32).reshape(B, Skv // ps)).to(dev)
+        sl = torch.full((B,), Skv, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, av.attn_decode_paged_workspace_bytes(B, Hq, Hkv, 1, D, ps, Skv // ps)),
+                         dtype=torch.uint8, device=dev)
+        _, per = time_launches([lambda: av.attn_decode_paged_fwd(q, kc, vc, bt, sl, score_mod="softcap",
+                                                                  mask="causal", out=out, workspace=ws)],
+                               steps, warmup)
+        byts = 2 * (2 * B * Hkv * Skv * D + 2 * B * Hq * D)
+        emit({"kernel": "attn_decode_paged_fwd", "score_mod": "softcap", "mask": "causal", "B": B, "Hq": Hq,
+              "Hkv": Hkv, "Sq": 1, "Skv": Skv, "page_size": ps, "D": D, "us": round(per[0] * 1e3, 2),
+              "hbm_gbs": round(byts / (per[0] * 1e-3) / 1e9, 1), "frac_hbm_peak": round(byts / (per[0] * 1e-3) / 8e12, 4)})
     for Nr in (256, 384, 768):
         Ns, Cm, Hh, dh = 128, 256, 8, 32
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)

@@ -14,6 +14,7 @@ from .attention import (  # noqa: F401
     allowed_matrix,
     softmax_two_pass,
     attention,
+    attention_backward,
     paged_decode_attention,
     diff_attention,
     sigmoid,

@@ -226,6 +226,56 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, *, page_s
     return out, lse
 
 
+def attention_backward(q, k, v, dout, *, score_mod: str = "none", mask: str = "none", scale: float | None = None,
+                       softcap: float = 20.0, alibi_max_bias: float = 8.0, window: int = 256, prefix_len: int = 0,
+                       doc_id=None):
+    """Gradients of ``attention`` (output only, not lse) for an upstream dout.
+
+    The pages name training as the extension of their method (talk notes,
+    "Background and motivation": attention is a bottleneck of training and
+    inference).  This is the chain rule of the plain definition, in float64:
+      t = mod(scale * q k^T), masked entries -inf;  p = softmax(t);  o = p v
+      dv = p^T dout                     (summed over the query heads of a KV head)
+      dp = dout v^T;  dt = p * (dp - rowsum(dp * p))
+      ds = dt * mod'(scale * q k^T)     (softcap: 1 - tanh(s/cap)^2; ALiBi and none: 1)
+      dq = scale * ds k;  dk = scale * ds^T q   (dk summed like dv)
+    Returns (dq [B,Hq,Sq,D], dk [B,Hkv,Skv,D], dv [B,Hkv,Skv,Dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    if mask != "none" and Sq != Skv:
+        raise ValueError("masks need Sq == Skv")
+    g = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.arange(Sq)
+    cols = np.arange(Skv)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        doc_row = None if doc_id is None else np.asarray(doc_id)[b]
+        for hq in range(Hq):
+            hk = hq // g
+            s = raw_scores(q[b, hq], k[b, hk], scale)
+            slope = alibi_slope(hq, Hq, alibi_max_bias)
+            t = apply_score_mod(s, score_mod, rows, cols, slope=slope, softcap=softcap)
+            a = allowed_matrix(mask, rows, Skv, window=window, prefix_len=prefix_len, doc_row=doc_row)
+            p, _ = softmax_two_pass(t, a)
+            dv[b, hk] += p.T @ dout[b, hq]
+            dp = dout[b, hq] @ v[b, hk].T
+            dt = p * (dp - np.sum(dp * p, axis=1, keepdims=True))
+            if score_mod == "softcap":
+                dt = dt * (1.0 - np.tanh(s / softcap) ** 2)
+            dq[b, hq] = scale * (dt @ k[b, hk])
+            dk[b, hk] += scale * (dt.T @ q[b, hq])
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # Differential attention.  The pages name it among the variants that
 # templates cannot express (talk notes, "Background and motivation" and

@@ -523,6 +523,58 @@ def test_paged_decode_pins():
     np.testing.assert_allclose(out2, out1, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("score_mod", ["none", "alibi", "softcap"])
+@pytest.mark.parametrize("mask", ["none", "causal", "sliding_window", "prefix_lm", "document"])
+def test_backward_matches_finite_differences(score_mod, mask):
+    """Central differences of L = sum(out * dout) in float64 pin every gradient
+    entry of the backward oracle (GQA 4/2, tiny shapes, softcap cap 2 so that
+    the tanh derivative matters)."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 6, 3
+    q = _rand((B, Hq, S, D), 90)
+    k = _rand((B, Hkv, S, D), 91)
+    v = _rand((B, Hkv, S, D), 92)
+    dout = _rand((B, Hq, S, D), 93)
+    kw = dict(score_mod=score_mod, mask=mask, softcap=2.0, alibi_max_bias=8.0, window=3, prefix_len=2,
+              doc_id=np.array([[0, 0, 1, 1, 1, 2]]))
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, **kw)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention(qq, kk, vv, **kw)
+        return float(np.sum(o * dout))
+
+    eps = 1e-6
+    for x, gx, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(gx, num, rtol=1e-6, atol=1e-7)
+
+
+def test_backward_reductions():
+    """GQA gradients equal the repeated-MHA gradients summed per KV head; with
+    q = 0 (uniform attention, no mask) dv is the column mean of dout."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 9, 5
+    q = _rand((B, Hq, S, D), 94)
+    k = _rand((B, Hkv, S, D), 95)
+    v = _rand((B, Hkv, S, D), 96)
+    dout = _rand((B, Hq, S, D), 97)
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, mask="causal")
+    kr, vr = np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1)
+    dq2, dk2, dv2 = oracle.attention_backward(q, kr, vr, dout, mask="causal")
+    np.testing.assert_allclose(dq, dq2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, dk2.reshape(B, Hkv, 2, S, D).sum(2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv2.reshape(B, Hkv, 2, S, D).sum(2), rtol=0, atol=1e-12)
+    _, _, dv0 = oracle.attention_backward(np.zeros_like(q), k, v, dout)
+    want = dout.reshape(B, Hkv, 2, S, D).sum(2).mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(dv0, np.broadcast_to(want, dv0.shape), rtol=0, atol=1e-12)
+
+
 def _evo_ungated(m, wq, wk, wv, bias, H, dh):
     """Independent loop form: per sequence, head and row."""
     Ns, Nr, _ = m.shape
