@@ -38,6 +38,8 @@ EXPORTED = (
     "attn_decode_fwd",
     "attn_decode_paged_workspace_bytes",
     "attn_decode_paged_fwd",
+    "attn_bwd_workspace_bytes",
+    "attn_bwd",
     "diff_attn_fwd",
     "evoformer_workspace_bytes",
     "evoformer_gated_attn_fwd",
@@ -91,6 +93,11 @@ def load_library(path: str | None = None):
     lib.attn_decode_paged_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                           ctypes.c_size_t, _i, _i, _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_decode_paged_fwd.restype = _i
+    lib.attn_bwd_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             ctypes.c_size_t, _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_bwd.restype = _i
     lib.diff_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp]
     lib.diff_attn_fwd.restype = _i
     lib.evoformer_workspace_bytes.argtypes = [_i, _i, _i, _i]
@@ -264,6 +271,35 @@ def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_m
                                    max_pages, num_pages, _stream_ptr(q.device))
     _check(rc, "attn_decode_paged_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
+             alibi_max_bias=8.0, kv_group=0, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of attn_fwd's output for an upstream ``dout``; ``lse``
+    is attn_fwd's (``return_lse=True``).  Masks: none or causal."""
+    import torch
+
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4)
+    _need(lse, "lse", torch.float32, 3)
+    B, Hq, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("dout must match q, lse must be [B, Hq, Sq]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
+                       kv_group=kv_group)
+    rc = lib.attn_bwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                      workspace.numel(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def diff_attn_fwd(q, k, v, *, lam=0.8, scale=0.0, causal=True, out=None):

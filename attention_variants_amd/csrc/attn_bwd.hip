@@ -1,0 +1,423 @@
+// Attention backward for gfx950: dQ, dK, dV of attn_fwd's output.
+//
+// The pages name training as the other half of the workload their fused
+// kernels serve (talk notes "Flashlight: PyTorch Compiler Extensions to
+// Accelerate Attention Variants", "Background and motivation").  The
+// arithmetic is the chain rule of the forward definition, recomputing P
+// instead of storing it:
+//   t = mod(scale q.k) (+ mask),  P = softmax(t)
+//   dV = P^T dO,   dP = dO V^T,   dT = P (dP - Delta),  Delta = rowsum(P dP)
+//   dS = dT mod'(scale q.k)   (softcap: 1 - tanh^2; none / ALiBi: 1)
+//   dQ = scale dS K,   dK = scale dS^T Q
+// Three launches over the same forward-shaped and key-owner layouts:
+//  1. row statistics: per query row, with the forward's lse only as an
+//     exponent reference, l = sum exp(t - lse) and Delta = sum exp(t - lse) dP / l,
+//     stored as a corrected reference (lse + ln l, log2 units) and Delta.
+//     P recomputed against the corrected reference sums to one in fp32, so
+//     neither the forward's bf16 row sum nor its bf16 output enters the
+//     gradients (Delta from rowsum(dO O) with a bf16 O cancels badly where
+//     attention concentrates).
+//  2. dK and dV by workgroups that own a 128-key tile and stream the query
+//     tiles of every query head of the KV head;
+//  3. dQ by workgroups that own 128 query rows and stream the key tiles.
+// No atomics: every output element has one writer (deterministic).
+
+#include "attn_tile.hpp"
+#include "av_kernels.hpp"
+
+namespace av {
+namespace {
+
+constexpr int NT = 256;
+constexpr int D = 64;
+constexpr int NDS = D / 16;   // k-steps over the head dimension
+constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
+constexpr int CPR = D / 8;    // 16-byte chunks per row
+
+// Score pieces shared by both gradient kernels, for one element: raw q.k in
+// `s`, query position qp, key position kp.  Returns p = exp(t - lse) (0 when
+// masked) and writes the factor mod'(scale q.k) to `dmod`.
+template <int SM>
+__device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, float slope2, float& dmod) {
+  if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+    // t = cap2 - 2 cap2 u, u = 1 / (1 + 2^(s sc_k)); mod' = 1 - tanh^2 = 4 u (1 - u)
+    const float cap2 = a.softcap * kLog2e;
+    const float u = rcp_fast(1.f + exp2_fast(s * a.sc_k));
+    dmod = 4.f * u * (1.f - u);
+    return exp2_fast(fmaf(-2.f * cap2, u, cap2 - l2));
+  } else {
+    dmod = 1.f;
+    return exp2_fast(fmaf(s, a.c, slope2 - l2));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  Workgroup = 128 keys of one (b, KV head); wave w owns keys
+// k0 + 32 w .. +31, held in registers as the B operand of S = Q K^T and
+// dP = dO V^T (lane = key).  Query tiles of 64 rows (two 32-row blocks) of
+// every query head of the group are staged in LDS, row-major and swizzled,
+// and read two ways: rows for the A operand of S and dP, transposed for the
+// A operand of dV^T += dO^T P and dK^T += Q^T dS.
+template <int SM, bool CAUSAL>
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
+  constexpr int BQ = 64;
+  constexpr int QCH = BQ * CPR / NT;  // 16-byte chunks per thread per tensor
+  __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
+  __shared__ __attribute__((aligned(16))) bf16 Gs[2][BQ * D];  // dO
+  __shared__ __attribute__((aligned(16))) float Ls[2][BQ];     // lse in log2 units (+inf past Sq)
+  __shared__ __attribute__((aligned(16))) float Es[2][BQ];     // Delta
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int nKT = (a.Skv + 127) / 128;
+  const int L = xcd_remap(blockIdx.x, a.total);
+  const int kt = L % nKT;
+  const int bk = L / nKT;
+  const int hk = bk % a.Hkv, b = bk / a.Hkv;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + 32 * w;      // first key of this wave
+  const int key = kw0 + l32;        // this lane's key (column of S, dP)
+
+  const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
+  const auto krs = make_rsrc((const bf16*)a.k + kvoff, (uint32_t)a.Skv * D * 2);
+  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, (uint32_t)a.Skv * D * 2);
+  bf16x8 kreg[NDS], vreg[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    kreg[s] = __builtin_bit_cast(bf16x8, buf_load16(krs, (uint32_t)(key * D + s * 16 + hh * 8) * 2));
+    vreg[s] = __builtin_bit_cast(bf16x8, buf_load16(vrs, (uint32_t)(key * D + s * 16 + hh * 8) * 2));
+  }
+  f32x16 dkT[NDB], dvT[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dkT[db] = dvT[db] = f32x16{};
+  const TrLane<D> tl(lane);
+  const bool key_live = key < a.Skv;
+
+  // work items: (query head of the group, 64-row query tile); causal: only
+  // tiles that reach this workgroup's keys
+  const int nQT = (a.Sq + BQ - 1) / BQ;
+  const int qt_lo = CAUSAL ? k0 / BQ : 0;
+  const int per_head = max(nQT - qt_lo, 0);
+  const int n_items = a.g * per_head;
+
+  i32x4 qr[QCH], gr[QCH];
+  float lr = 0.f, er = 0.f;
+  auto gload = [&](int item) {
+    const int hq = hk * a.g + item / per_head;
+    const int qt = qt_lo + item % per_head;
+    const size_t qoff = ((size_t)b * a.Hq + hq) * (size_t)a.Sq * D;
+    const auto qrs = make_rsrc((const bf16*)a.q + qoff, (uint32_t)a.Sq * D * 2);
+    const auto grs = make_rsrc((const bf16*)a.dout + qoff, (uint32_t)a.Sq * D * 2);
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+      const int idx = tid + NT * c;
+      const uint32_t off = (uint32_t)((qt * BQ + idx / CPR) * D + (idx % CPR) * 8) * 2;
+      qr[c] = buf_load16(qrs, off);
+      gr[c] = buf_load16(grs, off);
+    }
+    if (tid < BQ) {
+      const int q = qt * BQ + tid;
+      const size_t r = ((size_t)b * a.Hq + hq) * a.Sq + q;
+      lr = q < a.Sq ? a.stats[2 * r] : __builtin_inff();
+      er = q < a.Sq ? a.stats[2 * r + 1] : 0.f;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < QCH; ++c) {
+      const int idx = tid + NT * c;
+      *(i32x4*)&Qs[buf][tr_tile_off<D>(idx / CPR, (idx % CPR) * 8)] = qr[c];
+      *(i32x4*)&Gs[buf][tr_tile_off<D>(idx / CPR, (idx % CPR) * 8)] = gr[c];
+    }
+    if (tid < BQ) {
+      Ls[buf][tid] = lr;
+      Es[buf][tid] = er;
+    }
+  };
+
+  if (n_items > 0) gload(0);
+  for (int it = 0; it < n_items; ++it) {
+    const int buf = it & 1;
+    sstore(buf);
+    __syncthreads();
+    if (it + 1 < n_items) gload(it + 1);
+    const int hq = hk * a.g + it / per_head;
+    const int qt = qt_lo + it % per_head;
+    const float slope2 =
+        SM == SM_ALIBI ? uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq)) : 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int qb0 = qt * BQ + 32 * blk;  // first query of the block
+      if (CAUSAL && kw0 > qb0 + 31) continue;  // every key of the wave after every query
+      if (!__builtin_amdgcn_readfirstlane((int)(kw0 < a.Skv))) continue;
+      // S = Q K^T, dP = dO V^T: lane = key, registers = queries qb0 + 8(j/4) + 4hh + j%4
+      f32x16 sc = {}, dp = {};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const int off = tr_tile_off<D>(32 * blk + l32, s * 16 + hh * 8);
+        sc = mfma32(*(const bf16x8*)&Qs[buf][off], kreg[s], sc);
+        dp = mfma32(*(const bf16x8*)&Gs[buf][off], vreg[s], dp);
+      }
+      bf16x8 phi[2], plo[2], dhi[2], dlo[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 l4 = *(const f32x4*)&Ls[buf][32 * blk + 8 * g4 + 4 * hh];
+        const f32x4 e4 = *(const f32x4*)&Es[buf][32 * blk + 8 * g4 + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * g4 + e;
+          const int q = qb0 + 8 * g4 + 4 * hh + e;
+          const float bias = SM == SM_ALIBI ? slope2 * (float)(key - q) : 0.f;
+          float dmod;
+          float p = bwd_prob<SM>(a, sc[j], l4[e], bias, dmod);
+          bool ok = key_live;
+          if constexpr (CAUSAL) ok = ok && (key <= q);
+          p = ok ? p : 0.f;
+          const float ds = p * (dp[j] - e4[e]) * dmod;
+          const bf16 ph = (bf16)p;
+          phi[j >> 3][j & 7] = ph;
+          plo[j >> 3][j & 7] = (bf16)(p - (float)ph);
+          const bf16 hi = (bf16)ds;
+          dhi[j >> 3][j & 7] = hi;
+          dlo[j >> 3][j & 7] = (bf16)(ds - (float)hi);
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (query k-steps in the register order).
+      // P and dS enter as bf16 hi + lo pairs: the sums over queries cancel
+      // strongly where attention concentrates, and one bf16 rounding of the
+      // operand would show in the result.
+#pragma unroll
+      for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const bf16x8 gt_ = vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl);
+          dvT[d2] = mfma32(gt_, phi[tt], dvT[d2]);
+          dvT[d2] = mfma32(gt_, plo[tt], dvT[d2]);
+          const bf16x8 qt_ = vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl);
+          dkT[d2] = mfma32(qt_, dhi[tt], dkT[d2]);
+          dkT[d2] = mfma32(qt_, dlo[tt], dkT[d2]);
+        }
+    }
+  }
+
+  // ---- dK = scale dK^T^T, dV: lane holds d = 32 d2 + 8(j/4) + 4hh + j%4 of key `key`
+  if (!key_live) return;
+  bf16* dkrow = (bf16*)a.dk + kvoff + (size_t)key * D;
+  bf16* dvrow = (bf16*)a.dv + kvoff + (size_t)key * D;
+#pragma unroll
+  for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 vk, vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vk[e] = (bf16)(dkT[d2][4 * g4 + e] * a.scale);
+        vv[e] = (bf16)dvT[d2][4 * g4 + e];
+      }
+      *(bf16x4*)(dkrow + d2 * 32 + 8 * g4 + 4 * hh) = vk;
+      *(bf16x4*)(dvrow + d2 * 32 + 8 * g4 + 4 * hh) = vv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  Workgroup = 128 query rows of one (b, query head), wave = 32 rows;
+// the forward's layout: S^T = K Q^T and dP^T = V dO^T with Q, dO held in
+// registers (lane = query), K and V tiles staged in LDS (swizzled), then
+// dQ^T += K^T dS^T with K^T read transposed.
+// STATS = true is launch 1 (row statistics): the same loop without the dQ
+// product, summing p and p * dP per row.
+template <int SM, bool CAUSAL, bool STATS>
+__global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
+  constexpr int BN = 64;
+  constexpr int NCH = BN * CPR / NT;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int nM = (a.Sq + 127) / 128;
+  const int L = xcd_remap(blockIdx.x, a.total_q);
+  const int mt_lin = L % nM;
+  const int bh = L / nM;
+  const int hq = bh % a.Hq, b = bh / a.Hq;
+  const int hk = hq / a.g;
+  const int mt = CAUSAL ? nM - 1 - mt_lin : mt_lin;  // heaviest query tiles first
+  const int q0 = mt * 128;
+  const int qw = q0 + 32 * __builtin_amdgcn_readfirstlane(w);
+  const int q = qw + l32;
+  const size_t qoff = ((size_t)b * a.Hq + hq) * (size_t)a.Sq * D;
+  const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
+  const auto qrs = make_rsrc((const bf16*)a.q + qoff, (uint32_t)a.Sq * D * 2);
+  const auto grs = make_rsrc((const bf16*)a.dout + qoff, (uint32_t)a.Sq * D * 2);
+  const auto krs = make_rsrc((const bf16*)a.k + kvoff, (uint32_t)a.Skv * D * 2);
+  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, (uint32_t)a.Skv * D * 2);
+  bf16x8 qreg[NDS], greg[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) {
+    qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, (uint32_t)(q * D + s * 16 + hh * 8) * 2));
+    greg[s] = __builtin_bit_cast(bf16x8, buf_load16(grs, (uint32_t)(q * D + s * 16 + hh * 8) * 2));
+  }
+  const bool q_live = q < a.Sq;
+  const size_t rrow = ((size_t)b * a.Hq + hq) * a.Sq + (q_live ? q : 0);
+  // exponent reference (log2 units) and Delta: the forward's lse in the
+  // statistics pass, the corrected pair afterwards
+  float l2 = __builtin_inff(), dl = 0.f;
+  if (q_live) {
+    if constexpr (STATS) {
+      l2 = a.lse[rrow] * kLog2e;
+    } else {
+      l2 = a.stats[2 * rrow];
+      dl = a.stats[2 * rrow + 1];
+    }
+  }
+  float psum = 0.f, pdsum = 0.f;  // statistics pass: this lane's half of the row
+  const float slope2 = SM == SM_ALIBI ? uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq)) : 0.f;
+
+  f32x16 dqT[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
+  const TrLane<D> tl(lane);
+
+  const int nKV = (a.Skv + BN - 1) / BN;
+  const int n_hi = CAUSAL ? min(nKV, (min(q0 + 127, a.Sq - 1)) / BN + 1) : nKV;
+  const int qwlast = min(qw + 31, a.Sq - 1);
+
+  i32x4 kr[NCH], vr[NCH];
+  auto gload = [&](int nt) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + NT * c;
+      const uint32_t off = (uint32_t)((nt * BN + idx / CPR) * D + (idx % CPR) * 8) * 2;
+      kr[c] = buf_load16(krs, off);
+      vr[c] = buf_load16(vrs, off);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + NT * c;
+      const int off = tr_tile_off<D>(idx / CPR, (idx % CPR) * 8);
+      *(i32x4*)&Ks[buf][off] = kr[c];
+      *(i32x4*)&Vs[buf][off] = vr[c];
+    }
+  };
+
+  if (n_hi > 0) gload(0);
+  for (int nt = 0; nt < n_hi; ++nt) {
+    const int buf = nt & 1;
+    sstore(buf);
+    __syncthreads();
+    if (nt + 1 < n_hi) gload(nt + 1);
+    const int n0 = nt * BN;
+    if (qw >= a.Sq) continue;
+    if (CAUSAL && n0 > qwlast) continue;
+    // S^T, dP^T: lane = query, registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
+    f32x16 sc[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = dp[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const int off = tr_tile_off<D>(kb * 32 + l32, s * 16 + hh * 8);
+        sc[kb] = mfma32(*(const bf16x8*)&Ks[buf][off], qreg[s], sc[kb]);
+        dp[kb] = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp[kb]);
+      }
+    }
+    bf16x8 dhi[4], dlo[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kp = n0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
+        float dmod;
+        float p = bwd_prob<SM>(a, sc[kb][j], l2, bias, dmod);
+        bool ok = kp < a.Skv;
+        if constexpr (CAUSAL) ok = ok && (kp <= q);
+        p = ok ? p : 0.f;
+        if constexpr (STATS) {
+          psum += p;
+          pdsum = fmaf(p, dp[kb][j], pdsum);
+        } else {
+          const float ds = p * (dp[kb][j] - dl) * dmod;
+          const bf16 hi = (bf16)ds;
+          dhi[kb * 2 + (j >> 3)][j & 7] = hi;
+          dlo[kb * 2 + (j >> 3)][j & 7] = (bf16)(ds - (float)hi);
+        }
+      }
+    if constexpr (!STATS) {
+      // dQ^T += K^T dS^T, dS as a bf16 hi + lo pair (the row of dS sums to
+      // zero, so the products cancel)
+#pragma unroll
+      for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bf16x8 kt_ = vt_operand<D>(Ks[buf], t, d2 * 32, tl);
+          dqT[d2] = mfma32(kt_, dhi[t], dqT[d2]);
+          dqT[d2] = mfma32(kt_, dlo[t], dqT[d2]);
+        }
+    }
+  }
+
+  if constexpr (STATS) {
+    const float lsum = xhalf_sum(psum), dsum = xhalf_sum(pdsum);
+    if (q_live && hh == 0) {
+      a.stats[2 * rrow] = lsum > 0.f ? l2 + __log2f(lsum) : __builtin_inff();
+      a.stats[2 * rrow + 1] = lsum > 0.f ? dsum / lsum : 0.f;
+    }
+    return;
+  }
+  if (!q_live) return;
+  bf16* dqrow = (bf16*)a.dq + qoff + (size_t)q * D;
+#pragma unroll
+  for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 vq;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vq[e] = (bf16)(dqT[d2][4 * g4 + e] * a.scale);
+      *(bf16x4*)(dqrow + d2 * 32 + 8 * g4 + 4 * hh) = vq;
+    }
+}
+
+__global__ __launch_bounds__(NT) void zero_fill_kernel(i32x4* p, size_t n16) {
+  const size_t i = (size_t)blockIdx.x * NT + threadIdx.x;
+  if (i < n16) p[i] = i32x4{0, 0, 0, 0};
+}
+
+template <int SM, bool CAUSAL>
+hipError_t launch_bwd2(const BwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, CAUSAL, true>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<SM, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, CAUSAL, false>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int SM>
+hipError_t launch_bwd1(const BwdArgs& a, int causal, hipStream_t stream) {
+  return causal ? launch_bwd2<SM, true>(a, stream) : launch_bwd2<SM, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)((n16 + NT - 1) / NT)), dim3(NT), 0, stream, (i32x4*)p, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int causal, hipStream_t stream) {
+  switch (score_mod) {
+    case SM_NONE: return launch_bwd1<SM_NONE>(a, causal, stream);
+    case SM_ALIBI: return launch_bwd1<SM_ALIBI>(a, causal, stream);
+    case SM_SOFTCAP: return launch_bwd1<SM_SOFTCAP>(a, causal, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace av

@@ -228,6 +228,76 @@ int attn_decode_paged_fwd(const av_variant* var, const void* q, const void* k_ca
   return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv < 0 || D <= 0) return 0;
+  return (size_t)B * Hq * Sq * 8;
+}
+
+int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+             int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
+  if (var == nullptr) return AV_ERR_NULL;
+  if ((Sq > 0 && (q == nullptr || dout == nullptr || lse == nullptr || dq == nullptr)) ||
+      (Skv > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
+    return AV_ERR_NULL;
+  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
+  if (var->mask != AV_MASK_NONE && var->mask != AV_MASK_CAUSAL) return AV_ERR_UNSUPPORTED;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return AV_ERR_SHAPE;
+  if (var->kv_group != 0 && var->kv_group != Hq / Hkv) return AV_ERR_SHAPE;
+  if (var->mask == AV_MASK_CAUSAL && Sq != Skv) return AV_ERR_SHAPE;
+  if (D != 64) return AV_ERR_UNSUPPORTED;
+  if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
+  if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return AV_ERR_ALIGN;
+  if ((uint64_t)(Sq + 128) * D * 2 > kMaxSliceBytes || (uint64_t)(Skv + 128) * D * 2 > kMaxSliceBytes)
+    return AV_ERR_TOO_LARGE;
+  const int64_t total = (int64_t)B * Hkv * ((Skv + 127) / 128);
+  const int64_t total_q = (int64_t)B * Hq * ((Sq + 127) / 128);
+  if (total > INT32_MAX || total_q > INT32_MAX || (int64_t)B * Hq * Sq > INT32_MAX) return AV_ERR_TOO_LARGE;
+  if (Sq == 0) {
+    // no query: every key gets a zero gradient
+    if (Skv > 0) {
+      const size_t n = (size_t)B * Hkv * Skv * D * 2;
+      if (av::launch_zero_fill(dk, n, stream) != hipSuccess || av::launch_zero_fill(dv, n, stream) != hipSuccess)
+        return AV_ERR_HIP;
+    }
+    return AV_OK;
+  }
+  const size_t need = (size_t)B * Hq * Sq * 8;
+  if (workspace == nullptr || workspace_bytes < need) return AV_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return AV_ERR_ALIGN;
+
+  av::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.stats = (float*)workspace;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.Skv = Skv;
+  a.g = Hq / Hkv;
+  a.total = (int)total;
+  a.total_q = (int)total_q;
+  const double scale = var->scale > 0.f ? (double)var->scale : 1.0 / sqrt((double)D);
+  a.scale = (float)scale;
+  a.c = (float)(scale * kLog2e);
+  a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
+  a.sc_k = (float)(2.0 * scale * kLog2e / a.softcap);
+  a.alibi_max_bias = var->alibi_max_bias;
+  return hip_status(av::launch_attn_bwd(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
+}
+
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,
                   float lambda, float scale, int causal, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;

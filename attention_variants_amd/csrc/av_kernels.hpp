@@ -88,6 +88,31 @@ DecodePlan decode_plan(int B, int Hkv, int Skv);
 size_t decode_workspace_bytes(int B, int Hkv, int Skv, int D);
 hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream);
 
+// Attention backward (D = 64; masks none / causal).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;   // forward log-sum-exp, natural log, [B, Hq, Sq]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* stats;       // workspace [B, Hq, Sq, 2]: corrected reference (log2 units), Delta
+  int B, Hq, Hkv, Sq, Skv, g;
+  int total;          // dK/dV workgroups: B * Hkv * ceil(Skv / 128)
+  int total_q;        // dQ workgroups: B * Hq * ceil(Sq / 128)
+  float c;            // scale * log2(e)
+  float scale;
+  float sc_k;         // softcap: 2 * scale * log2(e) / cap
+  float alibi_max_bias;
+  float softcap;
+};
+hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int causal, hipStream_t stream);
+// Zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel (no memset
+// node, so the call can sit in a captured graph).
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+
 struct DiffArgs {
   const void* q;
   const void* k;

@@ -142,6 +142,26 @@ int attn_decode_paged_fwd(const av_variant* variant, const void* q, const void* 
                           void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int D,
                           int page_size, int max_pages, int num_pages, hipStream_t stream);
 
+/* Attention backward: gradients of attn_fwd's output (the pages name
+ * training as the other half of the workload, talk notes "Background and
+ * motivation").  With t = mod(scale q.k) masked and P = softmax(t):
+ *   dV = P^T dO,  dP = dO V^T,  dT = P (dP - rowsum(P dP)),
+ *   dS = dT mod'(scale q.k)  (softcap: 1 - tanh^2(scale q.k / cap); else 1),
+ *   dQ = scale dS K,  dK = scale dS^T Q   (dK, dV summed over the query heads
+ *   of a KV head).
+ * Inputs: q, k, v as given to attn_fwd, attn_fwd's `lse` (natural log,
+ * [B, Hq, Sq], required: it serves as the exponent reference; a first pass
+ * renormalises P in fp32, so its bf16 rounding does not reach the gradients)
+ * and dout [B, Hq, Sq, D].  Outputs dq [B, Hq, Sq, D], dk, dv
+ * [B, Hkv, Skv, D], bf16 (fp32 accumulation).  `workspace` (device,
+ * caller-owned, 16-byte aligned) holds attn_bwd_workspace_bytes(...) bytes.
+ * Supported: D = 64; mask none or causal (causal needs Sq == Skv); every
+ * score modifier.  Deterministic (no atomics). */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
+int attn_bwd(const av_variant* variant, const void* q, const void* k, const void* v, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+             int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream);
+
 /* Differential attention forward (talk notes, "Background and motivation"
  * and "Evaluation: complex attention variants"; the pages name the variant
  * without a formula; the reading implemented is):

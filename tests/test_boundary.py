@@ -188,6 +188,27 @@ def test_paged_decode_rejections(lib):
     assert call(Sq=0) == 0
 
 
+def test_backward_rejections(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 16, 4, 100, 100, 64) == 2 * 16 * 100 * 8
+
+    def call(score_mod=0, mask=1, lse=0x70000, dq=0x80000, ws=0x200000, wsb=1 << 30, B=1, Hq=4, Hkv=2, Sq=128,
+             Skv=128, D=64):
+        var = av.AvVariant(score_mod, mask, 0.0, 20.0, 8.0, 256, 0, None, 0)
+        return lib.attn_bwd(ctypes.byref(var), P, P2, P3, P4, lse, dq, 0x90000, 0xA0000, ws, wsb, B, Hq,
+                            Hkv, Sq, Skv, D, None)
+
+    assert call(lse=None) == -1
+    assert call(dq=None) == -1
+    assert call(mask=2) == -3
+    assert call(Skv=64) == -2          # causal needs Sq == Skv
+    assert call(D=128) == -3
+    assert call(Hq=3) == -2
+    assert call(ws=None) == -5
+    assert call(wsb=8) == -5
+    assert call(dq=0x80000 + 4) == -4
+    assert call(lse=0x70000 + 2) == -4
+
+
 def test_evoformer_column_rejections(lib):
     def call(m=P, w=P2, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):
         if wsb is None:
