@@ -273,6 +273,10 @@ def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_m
     return (out, lse) if return_lse else out
 
 
+def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D))
+
+
 def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
              alibi_max_bias=8.0, kv_group=0, dq=None, dk=None, dv=None, workspace=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for an upstream ``dout``; ``lse``

@@ -295,6 +295,23 @@ def run_sweep(path, steps, warmup):
         emit({"kernel": "diff_attn_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "executed_tflops": round(tf * 1.5, 1),
               "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+    # backward at the headline shape (algorithmic work: 5 products of 2*S*S*D
+    # per head, i.e. 2.5x the forward's visible FLOPs)
+    for (sm, mk) in (("none", "none"), ("softcap", "causal")):
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        dout = _dev(wi.normal_bf16(5, (B, H, S, D), 1.0), dev)
+        out, lse = av.attn_fwd(q, k, v, score_mod=sm, mask=mk, return_lse=True)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(av.attn_bwd_workspace_bytes(B, H, H, S, S, D), dtype=torch.uint8, device=dev)
+        _, per = time_launches([lambda: av.attn_bwd(q, k, v, dout, lse, score_mod=sm, mask=mk, dq=dq, dk=dk, dv=dv,
+                                                    workspace=ws)], steps, warmup)
+        fl = 2.5 * attn_flops(B, H, S, D, mk)
+        tf = fl / (per[0] * 1e-3) / 1e12
+        emit({"kernel": "attn_bwd", "score_mod": sm, "mask": mk, "B": B, "H": H, "S": S, "D": D,
+              "us": round(per[0] * 1e3, 2), "algorithmic_tflops": round(tf, 1),
+              "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
     # decoding: one new query per sequence against its key/value cache
     # (LLaMA-3.2-1B attention shape: 32 query heads, 8 KV heads, D = 64)
     for (B, Skv) in ((64, 4096), (8, 16384), (1, 16384)):
