@@ -41,6 +41,7 @@ EXPORTED = (
     "attn_bwd_workspace_bytes",
     "attn_bwd",
     "diff_attn_fwd",
+    "diff_head_fwd",
     "evoformer_workspace_bytes",
     "evoformer_gated_attn_fwd",
     "evoformer_col_gated_attn_fwd",
@@ -100,6 +101,9 @@ def load_library(path: str | None = None):
     lib.attn_bwd.restype = _i
     lib.diff_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _vp]
     lib.diff_attn_fwd.restype = _i
+    lib.diff_head_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _f, _f, _i,
+                                  _vp]
+    lib.diff_head_fwd.restype = _i
     lib.evoformer_workspace_bytes.argtypes = [_i, _i, _i, _i]
     lib.evoformer_workspace_bytes.restype = ctypes.c_size_t
     lib.evoformer_gated_attn_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
@@ -230,6 +234,10 @@ def attn_decode_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softca
     return (out, lse) if return_lse else out
 
 
+def attn_decode_paged_workspace_bytes(B, Hq, Hkv, Sq, D, page_size, max_pages) -> int:
+    return int(load_library().attn_decode_paged_workspace_bytes(B, Hq, Hkv, Sq, D, page_size, max_pages))
+
+
 def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_mod="none", mask="none", scale=0.0,
                           softcap=20.0, alibi_max_bias=8.0, kv_group=0, return_lse=False, out=None, lse=None,
                           workspace=None):
@@ -322,6 +330,41 @@ def diff_attn_fwd(q, k, v, *, lam=0.8, scale=0.0, causal=True, out=None):
     rc = lib.diff_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, S, D2 // 2, Dv,
                            float(lam), float(scale or 0.0), int(bool(causal)), _stream_ptr(q.device))
     _check(rc, "diff_attn_fwd")
+    return out
+
+
+def diff_head_fwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, *, lambda_init, gamma=None, eps=1e-5,
+                  scale=0.0, causal=True, out=None):
+    """Full differential-attention head: the differential core with
+    lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init, then per-row RMSNorm
+    (weight ``gamma``, ones when None) times (1 - lambda_init).
+    q, k [B,H,S,2*Dh], v [B,H,S,Dv] bf16; lambda_* [Dh], gamma [Dv] float32 on
+    the same device -> out [B,H,S,Dv] bf16."""
+    import torch
+
+    lib = load_library()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4)
+    B, H, S, D2 = q.shape
+    if tuple(k.shape) != (B, H, S, D2) or v.shape[:3] != (B, H, S) or D2 % 2:
+        raise ValueError("shape mismatch")
+    Dv = v.shape[3]
+    for t, n in ((lambda_q1, "lambda_q1"), (lambda_k1, "lambda_k1"), (lambda_q2, "lambda_q2"),
+                 (lambda_k2, "lambda_k2")):
+        _need(t, n, torch.float32, 1)
+        if t.shape[0] != D2 // 2 or t.device != q.device:
+            raise ValueError(f"{n} must be [Dh] on the device of q")
+    if gamma is not None:
+        _need(gamma, "gamma", torch.float32, 1)
+        if gamma.shape[0] != Dv or gamma.device != q.device:
+            raise ValueError("gamma must be [Dv] on the device of q")
+    if out is None:
+        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=q.device)
+    rc = lib.diff_head_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), lambda_q1.data_ptr(), lambda_k1.data_ptr(),
+                           lambda_q2.data_ptr(), lambda_k2.data_ptr(), None if gamma is None else gamma.data_ptr(),
+                           out.data_ptr(), B, H, S, D2 // 2, Dv, float(lambda_init), float(eps), float(scale or 0.0),
+                           int(bool(causal)), _stream_ptr(q.device))
+    _check(rc, "diff_head_fwd")
     return out
 
 

@@ -19,6 +19,36 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int hip_status(hipError_t e) { return e == hipSuccess ? AV_OK : AV_ERR_HIP; }
 
+// Shared validation and launch of the differential forms; `a` arrives with
+// the form's own fields (lambda, or the head parameters) already set.
+int diff_launch(av::DiffArgs& a, const void* q, const void* k, const void* v, void* out, int B, int H, int S,
+                int Dh, int Dv, float scale, int causal, hipStream_t stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
+  if (B <= 0 || H <= 0 || S < 0 || Dh <= 0 || Dv <= 0) return AV_ERR_SHAPE;
+  if (Dh != 64 || (Dv != 64 && Dv != 128)) return AV_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
+  if ((uint64_t)(S + av::kAttnBM) * 2 * Dh * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  if ((uint64_t)(S + av::kAttnBM) * Dv * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  const int64_t nM = ((int64_t)S + av::kAttnBM - 1) / av::kAttnBM;
+  const int64_t total = (int64_t)B * H * nM;
+  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
+  if (total == 0) return AV_OK;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.B = B;
+  a.H = H;
+  a.S = S;
+  a.nM = (int)nM;
+  a.total = (int)total;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
+  a.c = (float)(sc * kLog2e);
+  a.causal = causal != 0;
+  return hip_status(av::launch_diff_attn_fwd(a, Dv, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -300,33 +330,30 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
 
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,
                   float lambda, float scale, int causal, hipStream_t stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
-  if (B <= 0 || H <= 0 || S < 0 || Dh <= 0 || Dv <= 0) return AV_ERR_SHAPE;
-  if (Dh != 64 || (Dv != 64 && Dv != 128)) return AV_ERR_UNSUPPORTED;
   if (!isfinite(lambda)) return AV_ERR_PARAM;
-  if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
-  if ((uint64_t)(S + av::kAttnBM) * 2 * Dh * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
-  if ((uint64_t)(S + av::kAttnBM) * Dv * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
-  const int64_t nM = ((int64_t)S + av::kAttnBM - 1) / av::kAttnBM;
-  const int64_t total = (int64_t)B * H * nM;
-  if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
-  if (total == 0) return AV_OK;
   av::DiffArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = out;
-  a.B = B;
-  a.H = H;
-  a.S = S;
-  a.nM = (int)nM;
-  a.total = (int)total;
-  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
-  a.c = (float)(sc * kLog2e);
   a.lambda = lambda;
-  a.causal = causal != 0;
-  return hip_status(av::launch_diff_attn_fwd(a, Dv, stream));
+  return diff_launch(a, q, k, v, out, B, H, S, Dh, Dv, scale, causal, stream);
+}
+
+int diff_head_fwd(const void* q, const void* k, const void* v, const float* lambda_q1, const float* lambda_k1,
+                  const float* lambda_q2, const float* lambda_k2, const float* gamma, void* out, int B, int H, int S,
+                  int Dh, int Dv, float lambda_init, float eps, float scale, int causal, hipStream_t stream) {
+  if (lambda_q1 == nullptr || lambda_k1 == nullptr || lambda_q2 == nullptr || lambda_k2 == nullptr)
+    return AV_ERR_NULL;
+  if (!isfinite(lambda_init) || !(isfinite(eps) && eps > 0.f)) return AV_ERR_PARAM;
+  if (!aligned(lambda_q1, 4) || !aligned(lambda_k1, 4) || !aligned(lambda_q2, 4) || !aligned(lambda_k2, 4) ||
+      (gamma != nullptr && !aligned(gamma, 4)))
+    return AV_ERR_ALIGN;
+  av::DiffArgs a{};
+  a.lam_q1 = lambda_q1;
+  a.lam_k1 = lambda_k1;
+  a.lam_q2 = lambda_q2;
+  a.lam_k2 = lambda_k2;
+  a.gamma = gamma;
+  a.lambda_init = lambda_init;
+  a.eps = eps;
+  return diff_launch(a, q, k, v, out, B, H, S, Dh, Dv, scale, causal, stream);
 }
 
 size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh) {

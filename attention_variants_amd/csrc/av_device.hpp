@@ -76,6 +76,12 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// sum over all 64 lanes (butterfly), result in every lane
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
 
 // Workgroups are handed to the 8 XCDs round-robin by block id.  Remap so
 // that XCD x processes one contiguous range of logical tiles: neighbouring

@@ -123,6 +123,16 @@ struct DiffArgs {
   float c;        // scale * log2(e)
   float lambda;
   int causal;
+  // full head form (lam_q1 != nullptr): lambda = exp(lq1.lk1) - exp(lq2.lk2)
+  // + lambda_init computed in the kernel from four fp32 [64] vectors, then
+  // the per-row RMS norm with the fp32 [Dv] weight gamma (nullable = ones)
+  // and the (1 - lambda_init) factor
+  const float* lam_q1;
+  const float* lam_k1;
+  const float* lam_q2;
+  const float* lam_k2;
+  const float* gamma;
+  float lambda_init, eps;
 };
 hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dv, hipStream_t stream);
 

@@ -14,6 +14,17 @@
 // both branches; each V^T operand read from LDS feeds both PV products.  The
 // two output accumulators (32 rows x Dv fp32 per wave each) are combined in
 // the epilogue: out = O1 / l1 - lambda * O2 / l2.
+//
+// Full head form (HEAD): the DiffTransformer head around that core, as the
+// published Differential Transformer defines it (Ye et al., 2024; the pages
+// name DiffTransformer under related work, talk notes "Related work").  The
+// kernel derives lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init from the
+// four 64-wide parameter vectors (one lane per component, a wave-wide sum),
+// keeps A = O1/l1 - lambda O2/l2 in fp32, and stores
+// (1 - lambda_init) * gamma * A / sqrt(mean(A^2) + eps) per row: each query
+// row's Dv values sit in one lane pair, so the row's sum of squares is an
+// in-register sum plus one cross-half swap, and nothing leaves the kernel
+// before the normalised bf16 row.
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
@@ -27,7 +38,7 @@ constexpr int NT = 256;
 constexpr int DH = 64;   // width of one Q/K half
 constexpr int DQ = 2 * DH;
 
-template <int DV>
+template <int DV, bool HEAD>
 __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) {
   constexpr int NDS = DH / 16;          // QK^T k-steps per branch
   constexpr int NDB = DV / 32;          // O^T d-blocks per branch
@@ -144,20 +155,46 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
     }
   }
 
-  // out = O1 / l1 - lambda * O2 / l2
+  // A = O1 / l1 - lambda * O2 / l2 (fp32, in place in o1)
+  float lam = a.lambda;
+  if constexpr (HEAD) {
+    const float d1 = wave_sum(a.lam_q1[lane] * a.lam_k1[lane]);
+    const float d2 = wave_sum(a.lam_q2[lane] * a.lam_k2[lane]);
+    lam = expf(d1) - expf(d2) + a.lambda_init;
+  }
   const float l1 = xhalf_sum(st1.l), l2 = xhalf_sum(st2.l);
   const float inv1 = l1 > 0.f ? 1.f / l1 : 0.f;
-  const float inv2 = l2 > 0.f ? a.lambda / l2 : 0.f;
+  const float inv2 = l2 > 0.f ? lam / l2 : 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o1[db][j] = fmaf(o1[db][j], inv1, -o2[db][j] * inv2);
+  // head form: (1 - lambda_init) / sqrt(mean(A^2) + eps) over the row's DV values
+  float post = 1.f;
+  if constexpr (HEAD) {
+    float ss = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) ss = fmaf(o1[db][j], o1[db][j], ss);
+    ss = xhalf_sum(ss);
+    post = (1.f - a.lambda_init) * rsqrtf(ss * (1.f / DV) + a.eps);
+  }
   if (qi < S) {
     bf16* orow = (bf16*)a.o + voff + (size_t)qi * DV;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = db * 32 + 8 * g4 + 4 * hh;
         bf16x4 val;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) val[e] = (bf16)fmaf(o1[db][g4 * 4 + e], inv1, -o2[db][g4 * 4 + e] * inv2);
-        *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = val;
+        for (int e = 0; e < 4; ++e) {
+          float y = o1[db][g4 * 4 + e];
+          if constexpr (HEAD) y *= post * (a.gamma != nullptr ? a.gamma[col + e] : 1.f);
+          val[e] = (bf16)y;
+        }
+        *(bf16x4*)(orow + col) = val;
       }
     }
   }
@@ -166,15 +203,18 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
 }  // namespace
 
 hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dv, hipStream_t stream) {
-  switch (Dv) {
-    case 64:
-      hipLaunchKernelGGL(diff_attn_fwd_kernel<64>, dim3(a.total), dim3(NT), 0, stream, a);
-      return hipGetLastError();
-    case 128:
-      hipLaunchKernelGGL(diff_attn_fwd_kernel<128>, dim3(a.total), dim3(NT), 0, stream, a);
-      return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
+  const bool head = a.lam_q1 != nullptr;
+  if (Dv == 64 && !head)
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<64, false>), dim3(a.total), dim3(NT), 0, stream, a);
+  else if (Dv == 64)
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<64, true>), dim3(a.total), dim3(NT), 0, stream, a);
+  else if (Dv == 128 && !head)
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<128, false>), dim3(a.total), dim3(NT), 0, stream, a);
+  else if (Dv == 128)
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<128, true>), dim3(a.total), dim3(NT), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace av

@@ -295,6 +295,14 @@ def run_sweep(path, steps, warmup):
         emit({"kernel": "diff_attn_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "executed_tflops": round(tf * 1.5, 1),
               "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+        # the full head (lambda re-parameterisation and per-row RMSNorm fused in the epilogue)
+        hp = {n: torch.from_numpy(a).to(dev) for n, a in wi.diff_head_params(64, 128).items()}
+        _, per = time_launches([lambda: av.diff_head_fwd(q, k, v, hp["lq1"], hp["lk1"], hp["lq2"], hp["lk2"],
+                                                         lambda_init=0.2, gamma=hp["gamma"], out=out)],
+                               steps, warmup)
+        tf = pairs * 512 / (per[0] * 1e-3) / 1e12
+        emit({"kernel": "diff_head_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
+              "visible_tflops": round(tf, 1), "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
     # backward at the headline shape (algorithmic work: 5 products of 2*S*S*D
     # per head, i.e. 2.5x the forward's visible FLOPs)
     for (sm, mk) in (("none", "none"), ("softcap", "causal")):

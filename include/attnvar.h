@@ -173,6 +173,25 @@ int attn_bwd(const av_variant* variant, const void* q, const void* k, const void
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh,
                   int Dv, float lambda, float scale, int causal, hipStream_t stream);
 
+/* Full differential-attention head (DiffTransformer, which the talk notes
+ * name under "Related work"; the pages benchmark only the attention core
+ * above).  The head follows the published Differential Transformer (Ye et
+ * al., 2024: differential attention and its multi-head form):
+ *   lambda = exp(lambda_q1 . lambda_k1) - exp(lambda_q2 . lambda_k2) + lambda_init
+ *   A      = the diff_attn_fwd result with that lambda, kept in fp32
+ *   out[b, h, i, e] = (1 - lambda_init) * gamma[e] * A[i, e] / sqrt(mean_e' A[i, e']^2 + eps)
+ * i.e. RMSNorm over the Dv channels of each row (per head), then the
+ * (1 - lambda_init) factor.  The published depth schedule is
+ * lambda_init = 0.8 - 0.6 exp(-0.3 (l - 1)) for 1-based layer l; the caller
+ * passes the value.  lambda_q1 .. lambda_k2: device fp32 [Dh] each; gamma:
+ * device fp32 [Dv] or NULL (all ones); all 4-byte aligned, caller-owned.
+ * The kernel computes lambda on the device, so the parameters may change
+ * between calls without a host round trip.  q, k, v, out, shapes, scale,
+ * causal and support as diff_attn_fwd.  eps must be finite and > 0. */
+int diff_head_fwd(const void* q, const void* k, const void* v, const float* lambda_q1, const float* lambda_k1,
+                  const float* lambda_q2, const float* lambda_k2, const float* gamma, void* out, int B, int H, int S,
+                  int Dh, int Dv, float lambda_init, float eps, float scale, int causal, hipStream_t stream);
+
 /* Evoformer row-wise gated self-attention with pair bias (talk notes,
  * "Evaluation: complex attention variants" and the AlphaFold2 end-to-end
  * section; no formula on the pages; the reading implemented is, per MSA

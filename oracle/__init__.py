@@ -17,6 +17,9 @@ from .attention import (  # noqa: F401
     attention_backward,
     paged_decode_attention,
     diff_attention,
+    diff_lambda_init,
+    diff_lambda,
+    diff_head,
     sigmoid,
     evoformer_projections,
     evoformer_row_gated_attention,

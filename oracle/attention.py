@@ -314,6 +314,40 @@ def diff_attention(q, k, v, *, lam: float = 0.8, scale: float | None = None,
 
 
 # --------------------------------------------------------------------------
+# The full differential-attention head.  The pages name DiffTransformer among
+# the flexible attention models that motivate the work (talk notes, "Related
+# work") and benchmark only its attention core.  The head around that core is
+# taken from the published Differential Transformer (Ye et al., 2024, the
+# sections on differential attention and on its multi-head form):
+#   lambda         = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init
+#   A              = (softmax(s Q1 K1^T) - lambda softmax(s Q2 K2^T)) V
+#   y[i, e]        = (1 - lambda_init) * gamma[e] * A[i, e] / sqrt(mean_e' A[i, e']^2 + eps)
+#   lambda_init(l) = 0.8 - 0.6 exp(-0.3 (l - 1)),   l = 1-based layer index
+# The per-head normalisation is RMSNorm over the Dv channels of each row with
+# a per-channel weight gamma (ones when absent).  The output projection over
+# the concatenated heads is a plain GEMM and not part of the head.
+# --------------------------------------------------------------------------
+def diff_lambda_init(layer: int) -> float:
+    return 0.8 - 0.6 * math.exp(-0.3 * (layer - 1))
+
+
+def diff_lambda(lq1, lk1, lq2, lk2, lambda_init: float) -> float:
+    d1 = float(np.dot(np.asarray(lq1, dtype=np.float64), np.asarray(lk1, dtype=np.float64)))
+    d2 = float(np.dot(np.asarray(lq2, dtype=np.float64), np.asarray(lk2, dtype=np.float64)))
+    return math.exp(d1) - math.exp(d2) + lambda_init
+
+
+def diff_head(q, k, v, lq1, lk1, lq2, lk2, *, lambda_init: float, gamma=None, eps: float = 1e-5,
+              scale: float | None = None, causal: bool = True, rows=None):
+    lam = diff_lambda(lq1, lk1, lq2, lk2, lambda_init)
+    a = diff_attention(q, k, v, lam=lam, scale=scale, causal=causal, rows=rows)
+    Dv = a.shape[-1]
+    g = np.ones(Dv) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    rms = np.sqrt(np.mean(a * a, axis=-1, keepdims=True) + eps)
+    return (1.0 - lambda_init) * g * (a / rms)
+
+
+# --------------------------------------------------------------------------
 # Evoformer row-wise gated self-attention with pair bias.  The pages name it
 # (talk notes, "Background and motivation", "Evaluation: complex attention
 # variants", and the AlphaFold2 end-to-end section: 8 heads x 32) without a

@@ -112,6 +112,31 @@ def test_diff_attn_rejections(lib):
     assert call(S=0) == 0
 
 
+def test_diff_head_rejections(lib):
+    L1, L2, L3, L4, G = 0x50000, 0x50100, 0x50200, 0x50300, 0x50400
+
+    def call(q=P, k=P2, v=P3, lq1=L1, lk1=L2, lq2=L3, lk2=L4, gamma=G, o=P4, B=1, H=2, S=64, Dh=64, Dv=128,
+             lam_init=0.2, eps=1e-5, scale=0.0):
+        return lib.diff_head_fwd(q, k, v, lq1, lk1, lq2, lk2, gamma, o, B, H, S, Dh, Dv, lam_init, eps, scale, 1,
+                                 None)
+
+    assert call(q=None) == -1
+    assert call(lq1=None) == -1
+    assert call(lk2=None) == -1
+    assert call(B=0) == -2
+    assert call(Dh=32) == -3
+    assert call(Dv=96) == -3
+    assert call(lam_init=float("inf")) == -7
+    assert call(eps=0.0) == -7
+    assert call(eps=-1e-5) == -7
+    assert call(eps=float("nan")) == -7
+    assert call(lk1=L2 + 2) == -4
+    assert call(gamma=G + 1) == -4
+    assert call(v=P3 + 8) == -4
+    assert call(S=0) == 0
+    assert call(S=0, gamma=None) == 0
+
+
 def test_evoformer_rejections(lib):
     need = lib.evoformer_workspace_bytes(128, 256, 8, 32)
     assert need == 4 * 128 * 256 * 8 * 32 * 2
@@ -242,3 +267,11 @@ def test_python_binding_rejects_cpu_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError):
         av.load_library(str(tmp_path / "nope.so"))
+
+
+def test_binding_has_every_exported_function():
+    """Each C entry point has a Python function of the same name in the binding."""
+    for name in av.EXPORTED:
+        if name.startswith("av_"):
+            continue
+        assert callable(getattr(av, name, None)), name

@@ -379,6 +379,100 @@ def test_p7_diff_reductions():
     np.testing.assert_allclose(oracle.diff_attention(q, k, v, lam=0.8)[:, :, 0], 0.2 * v[:, :, 0], atol=1e-12)
 
 
+# ---------------------------------------------------------------- P7b: full differential head
+def _scalar_causal_attention(q, k, v, scale):
+    """One head, scalar loops, no max subtraction (tiny, well-scaled inputs)."""
+    S, d = q.shape
+    out = np.zeros((S, v.shape[1]))
+    for i in range(S):
+        w = [math.exp(scale * sum(q[i, t] * k[j, t] for t in range(d))) for j in range(i + 1)]
+        z = sum(w)
+        for e in range(v.shape[1]):
+            out[i, e] = sum(w[j] * v[j, e] for j in range(i + 1)) / z
+    return out
+
+
+def test_p7b_lambda_init_schedule():
+    # first layer 0.2, approaches 0.8 with depth, increasing
+    assert oracle.diff_lambda_init(1) == pytest.approx(0.2, abs=1e-15)
+    assert oracle.diff_lambda_init(200) == pytest.approx(0.8, abs=1e-12)
+    vals = [oracle.diff_lambda_init(l) for l in range(1, 25)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))
+
+
+def test_p7b_lambda_reparameterisation():
+    ln3 = math.log(3.0)
+    # exp(ln 3) - exp(0) + 0.2 = 2.2, and with the two pairs swapped 1 - 3 + 0.2
+    assert oracle.diff_lambda([ln3, 0, 0], [1, 0, 5], [0, 0, 0], [4, 4, 4], 0.2) == pytest.approx(2.2, abs=1e-12)
+    assert oracle.diff_lambda([0, 0, 0], [4, 4, 4], [ln3, 0, 0], [1, 0, 5], 0.2) == pytest.approx(-1.8, abs=1e-12)
+    # the dot product, not an elementwise or first-component product
+    assert oracle.diff_lambda([0.5, 0.25], [2.0, 4.0], [0, 0], [0, 0], 0.0) == pytest.approx(math.e ** 2 - 1, abs=1e-12)
+
+
+@pytest.mark.parametrize("a,b,lam_init,eps", [
+    (math.log(1.9), 0.0, 0.2, 0.0),   # lambda = 1.1: the head flips the sign of attention
+    (0.0, math.log(1.5), 0.2, 0.0),   # lambda = -0.3: same sign
+    (math.log(1.9), 0.0, 0.0, 0.0),   # without lambda_init, lambda = 0.9: same sign
+    (0.0, math.log(1.5), 0.35, 0.3),  # eps matters: the magnitude of (1 - lambda) survives the norm
+])
+def test_p7b_identical_halves_closed_form(a, b, lam_init, eps):
+    """Q2 = Q1, K2 = K1 make A = (1 - lambda) attn(Q1, K1, V); with attention
+    from scalar loops, y = (1 - lambda_init) gamma (1 - lambda) attn / sqrt((1 - lambda)^2 mean(attn^2) + eps)."""
+    S, Dh, Dv = 6, 3, 4
+    q1, k1, v = _rand((S, Dh), 80) * 0.7, _rand((S, Dh), 81) * 0.7, _rand((S, Dv), 82)
+    gamma = 1.0 + 0.3 * _rand(Dv, 83)
+    q = np.concatenate([q1, q1], axis=-1)[None, None]
+    k = np.concatenate([k1, k1], axis=-1)[None, None]
+    lq1, lk1 = np.array([a, 0.0, 0.0]), np.array([1.0, 2.0, 3.0])
+    lq2, lk2 = np.array([0.0, 7.0, 0.0]), np.array([9.0, b / 7.0, 1.0])  # lq2 . lk2 = b
+    lam = math.exp(a) - math.exp(b) + lam_init
+    y = oracle.diff_head(q, k, v[None, None], lq1, lk1, lq2, lk2, lambda_init=lam_init, gamma=gamma, eps=eps)
+    att = _scalar_causal_attention(q1, k1, v, 1 / math.sqrt(Dh))
+    A = (1.0 - lam) * att
+    want = np.zeros((S, Dv))
+    for i in range(S):
+        rms = math.sqrt(sum(x * x for x in A[i]) / Dv + eps)
+        for e in range(Dv):
+            want[i, e] = (1.0 - lam_init) * gamma[e] * A[i, e] / rms
+    np.testing.assert_allclose(y[0, 0], want, rtol=0, atol=1e-12)
+    if eps == 0.0:  # sign of (1 - lambda) decides the sign of every output
+        assert np.all(np.sign(y[0, 0] * gamma * att) == np.sign(1.0 - lam))
+
+
+def test_p7b_row_rms_and_gamma():
+    """With eps = 0 and gamma = 1 every output row has RMS |1 - lambda_init|;
+    gamma multiplies channelwise after the norm."""
+    S, Dh, Dv = 41, 8, 12
+    q, k, v = _rand((2, 3, S, 2 * Dh), 84), _rand((2, 3, S, 2 * Dh), 85), _rand((2, 3, S, Dv), 86)
+    lv = [0.3 * _rand(Dh, 87 + i) for i in range(4)]
+    y = oracle.diff_head(q, k, v, *lv, lambda_init=0.35, eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 0.65, rtol=1e-12)
+    gamma = 1.0 + 0.2 * _rand(Dv, 91)
+    yg = oracle.diff_head(q, k, v, *lv, lambda_init=0.35, eps=0.0, gamma=gamma)
+    np.testing.assert_allclose(yg, y * gamma, rtol=1e-12, atol=1e-14)
+    # the norm removes any positive scale of V
+    np.testing.assert_allclose(oracle.diff_head(q, k, 7.5 * v, *lv, lambda_init=0.35, eps=0.0), y, rtol=1e-10)
+
+
+def test_p7b_scalar_brute_force():
+    """The whole head by scalar loops on a tiny input (distinct halves)."""
+    S, Dh, Dv = 5, 2, 3
+    q, k, v = _rand((S, 2 * Dh), 92), _rand((S, 2 * Dh), 93), _rand((S, Dv), 94)
+    lq1, lk1, lq2, lk2 = (0.4 * _rand(Dh, 95 + i) for i in range(4))
+    gamma, lam_init, eps = 1.0 + 0.3 * _rand(Dv, 99), 0.45, 1e-3
+    y = oracle.diff_head(q[None, None], k[None, None], v[None, None], lq1, lk1, lq2, lk2,
+                         lambda_init=lam_init, gamma=gamma, eps=eps)
+    lam = (math.exp(sum(lq1[t] * lk1[t] for t in range(Dh))) - math.exp(sum(lq2[t] * lk2[t] for t in range(Dh)))
+           + lam_init)
+    a1 = _scalar_causal_attention(q[:, :Dh], k[:, :Dh], v, 1 / math.sqrt(Dh))
+    a2 = _scalar_causal_attention(q[:, Dh:], k[:, Dh:], v, 1 / math.sqrt(Dh))
+    for i in range(S):
+        A = [a1[i, e] - lam * a2[i, e] for e in range(Dv)]
+        rms = math.sqrt(sum(x * x for x in A) / Dv + eps)
+        for e in range(Dv):
+            assert y[0, 0, i, e] == pytest.approx((1 - lam_init) * gamma[e] * A[e] / rms, abs=1e-12)
+
+
 # ---------------------------------------------------------------- P8
 def test_p8_evoformer_reductions():
     Ns, Nr, Cm, H, dh = 3, 11, 16, 2, 4

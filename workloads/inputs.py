@@ -119,6 +119,17 @@ def diff_inputs(B, H, S, Dh=64, Dv=128, seeds=(1, 2, 3)):
     }
 
 
+def diff_head_params(Dh=64, Dv=128, seed=17):
+    """Parameters of a differential-attention head, float32: the four lambda
+    vectors ``[Dh]`` ~ N(0, 0.1^2) (the published initialisation) and a
+    per-channel norm weight ``gamma [Dv]`` ~ N(1, 0.1^2) (ones at
+    initialisation; drawn here so that every channel's weight matters)."""
+    rng = np.random.default_rng(seed)
+    out = {n: (0.1 * rng.standard_normal(Dh)).astype(np.float32) for n in ("lq1", "lk1", "lq2", "lk2")}
+    out["gamma"] = (1.0 + 0.1 * rng.standard_normal(Dv)).astype(np.float32)
+    return out
+
+
 def evoformer_inputs(Ns, Nr, Cm=256, H=8, dh=32, seeds=None):
     """MSA activations ``m [Ns,Nr,Cm]`` ~ N(0,1); four projection weights
     ``[Cm, H*dh]`` ~ N(0, 1/Cm) (variance 1/Cm); pair bias ``[H,Nr,Nr]`` ~ N(0,1)."""
