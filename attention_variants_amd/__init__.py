@@ -15,7 +15,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnvar.so")
 
-SCORE_MODS = {"none": 0, "alibi": 1, "softcap": 2}
+SCORE_MODS = {"none": 0, "alibi": 1, "softcap": 2, "bias": 3}
 MASKS = {"none": 0, "causal": 1, "sliding_window": 2, "prefix_lm": 3, "document": 4}
 
 AV_OK = 0
@@ -63,6 +63,9 @@ class AvVariant(ctypes.Structure):
         ("prefix_len", ctypes.c_int32),
         ("doc_id", ctypes.c_void_p),
         ("kv_group", ctypes.c_int32),
+        ("bias", ctypes.c_void_p),
+        ("bias_batch_stride", ctypes.c_int64),
+        ("bias_head_stride", ctypes.c_int64),
     ]
 
 
@@ -152,20 +155,24 @@ def _need(t, name, dtype, ndim):
 
 
 def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alibi_max_bias=8.0,
-                 window=256, prefix_len=0, doc_id=None, kv_group=0) -> AvVariant:
+                 window=256, prefix_len=0, doc_id=None, kv_group=0, bias=None, bias_batch_stride=0,
+                 bias_head_stride=0) -> AvVariant:
     if score_mod not in SCORE_MODS:
         raise ValueError(f"unknown score_mod {score_mod!r}")
     if mask not in MASKS:
         raise ValueError(f"unknown mask {mask!r}")
     return AvVariant(SCORE_MODS[score_mod], MASKS[mask], float(scale or 0.0), float(softcap),
                      float(alibi_max_bias), int(window), int(prefix_len),
-                     None if doc_id is None else int(doc_id.data_ptr()), int(kv_group))
+                     None if doc_id is None else int(doc_id.data_ptr()), int(kv_group),
+                     None if bias is None else int(bias.data_ptr()), int(bias_batch_stride), int(bias_head_stride))
 
 
 def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0, alibi_max_bias=8.0,
-             window=256, prefix_len=0, doc_id=None, kv_group=0, return_lse=False, out=None, lse=None):
+             window=256, prefix_len=0, doc_id=None, kv_group=0, bias=None, return_lse=False, out=None, lse=None):
     """Fused attention forward.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] bf16 -> out [B,Hq,Sq,D] (bf16).
 
+    ``score_mod="bias"`` adds ``bias`` (bf16 [Bb, Hb, Sq, Skv], Bb in {1, B},
+    Hb in {1, Hq}; a size-1 axis is shared) to the scaled scores.
     With ``return_lse`` also returns the fp32 natural-log sum-exp per row.
     """
     import torch
@@ -181,6 +188,18 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
         _need(doc_id, "doc_id", torch.int32, 2)
         if tuple(doc_id.shape) != (B, Sq):
             raise ValueError("doc_id must be [B, S]")
+    bs = hs = 0
+    if score_mod == "bias":
+        if bias is None:
+            raise ValueError("score_mod='bias' needs a bias tensor")
+        _need(bias, "bias", torch.bfloat16, 4)
+        Bb, Hb = bias.shape[:2]
+        if Bb not in (1, B) or Hb not in (1, Hq) or tuple(bias.shape[2:]) != (Sq, Skv):
+            raise ValueError(f"bias must be [1 or B, 1 or Hq, Sq, Skv], got {tuple(bias.shape)}")
+        hs = Sq * Skv if Hb > 1 else 0
+        bs = Hb * Sq * Skv if Bb > 1 else 0
+    elif bias is not None:
+        raise ValueError("bias given without score_mod='bias'")
     if out is None:
         out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
     else:
@@ -188,7 +207,8 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
     if return_lse and lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
-                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group)
+                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group, bias=bias,
+                       bias_batch_stride=bs, bias_head_stride=hs)
     rc = lib.attn_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       None if lse is None else lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
     _check(rc, "attn_fwd")

@@ -57,16 +57,18 @@ constexpr int BN = 64;   // keys per KV tile
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 
 // Waves per SIMD each instantiation's register budget is sized for: two
-// with two query blocks per wave or D = 128, three with one block.
+// with two query blocks per wave, D = 128 or the bias tensor at D = 64 (its
+// prefetched bias tile does not fit a third wave's budget), three otherwise.
 template <int D, int SM, int MK>
 constexpr int min_waves() {
-  return attn_qb(D, MK) == 2 || D == 128 ? 2 : 3;
+  return attn_qb(D, SM, MK) == 2 || D == 128 || (SM == SM_TBIAS && D == 64) ? 2 : 3;
 }
 
 template <int D, int SM, int MK>
 __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int QB = attn_qb(D, MK);  // 32-row query blocks per wave
-  constexpr int BM = attn_bm(D, MK);  // query rows per workgroup
+  constexpr int QB = attn_qb(D, SM, MK);  // 32-row query blocks per wave
+  constexpr int BM = attn_bm(D, SM, MK);  // query rows per workgroup
+  constexpr bool kBias = SM == SM_BIAS || SM == SM_TBIAS;  // a bias tile is read per KV tile
   constexpr int WQ = 32 * QB;        // query rows per wave
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
   constexpr int NDB = D / 32;        // 32-wide d blocks of O^T
@@ -213,9 +215,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
     for (int g = 0; g < NKB * 4; ++g) alibi_u[g] = uniform_f(alibi_slope2 * (float)(8 * g));
   }
-  // Evoformer pair bias of head hq: 4 keys (8 bytes) per load
-  const auto brs = make_rsrc(SM == SM_BIAS ? (const bf16*)a.bias + (size_t)hq * a.Sq * a.Skv : nullptr,
-                             SM == SM_BIAS ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
+  // bias slice of (b, hq) (Evoformer pair bias or bias tensor): 4 keys (8 bytes) per load
+  const auto brs = make_rsrc(kBias ? (const bf16*)a.bias + (size_t)b * a.bias_bs + (size_t)hq * a.bias_hs : nullptr,
+                             kBias ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
   // softcap in log2 units: cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k))
   // = cap2 - 1 / fma(E, invK, invK) with E = 2^(raw*sc_k), invK = 1/(2*cap2): one exp2,
   // one fma, one rcp; with the fixed reference the kernel keeps t - cap2
@@ -262,8 +264,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
   };
 
-  // Evoformer pair bias of this lane's (query, key) elements: keys
-  // n0 + 4*hh + 32*kb + 8*g + 0..3, loaded one tile ahead of its use
+  // bias of this lane's (query, key) elements: keys n0 + 4*hh + 32*kb +
+  // 8*g + 0..3, loaded one tile ahead of its use
   i32x4 braw[QB][NKB * 2];
   auto bias_load = [&](int n0) {
 #pragma unroll
@@ -290,9 +292,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
     }
   };
-  // exponent argument scale: scores of vanilla attention are raw q.k, pair-bias
+  // exponent argument scale: scores of vanilla attention are raw q.k, biased
   // scores are q.k*scale + bias (natural units); the other modifiers produce log2 units
-  const float cexp = SM == SM_BIAS ? kLog2e : a.c;
+  const float cexp = kBias ? kLog2e : a.c;
 
   // One KV tile for this wave.  Only the element mask depends on the tile
   // class, and it edits the score registers in place, so the MFMA
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // ---- score modifier: ALiBi and softcap in log2 units, pair bias in natural
+      // ---- score modifier: ALiBi and softcap in log2 units, bias in natural
       //      units (q.k*scale + bias); vanilla keeps the raw q.k, its scale folded into exp2
       if constexpr (SM != SM_NONE && SM != SM_GATE) {
         // ALiBi goes straight to the exponent argument, relative to the
@@ -336,7 +338,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
               s[qb][kb][j] = fmaf(s[qb][kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
             } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
               s[qb][kb][j] = softcap_t(s[qb][kb][j]);
-            } else {  // pair bias: bf16 -> fp32 is a 16-bit shift
+            } else {  // bias: bf16 -> fp32 is a 16-bit shift
               const int wd = braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
               const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
               s[qb][kb][j] = fmaf(s[qb][kb][j], a.scale, bv);
@@ -371,16 +373,12 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
     }
 
-    if constexpr (SM == SM_BIAS) {
-      if (n0 + BN < n_hi * BN) bias_load(n0 + BN);  // the next tile's bias, in flight during this one
-    }
-
     // ---- exponent reference and p = exp2(t - m_ref) -> bf16 P^T operands,
     //      with the row sum of the bf16 values
-    constexpr int MODE = (SM == SM_NONE || SM == SM_BIAS || SM == SM_GATE) ? 0
-                         : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
+    constexpr bool kOptimistic = SM == SM_NONE || kBias || SM == SM_GATE;
+    constexpr int MODE = kOptimistic ? 0 : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
     bf16x8 pb[QB][NPS];
-    if constexpr (SM == SM_NONE || SM == SM_BIAS || SM == SM_GATE) {
+    if constexpr (kOptimistic) {
       // Optimistic: exponentiate against the current reference and keep the
       // result unless some exponential exceeds 2^64 (then the tile sum does)
       // or the row has no reference yet.  The reference is only ever a
@@ -460,7 +458,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   };
 
   if (n_lo < n_hi) gload(n_lo);
-  if constexpr (SM == SM_BIAS) {
+  if constexpr (kBias) {
     if (n_lo < n_hi) bias_load(n_lo * BN);
   }
 
@@ -488,8 +486,12 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       skip |= (d1 < dqw) || (d0 > dqwlast);
       full &= (d0 == dqw) && (d1 == dqwlast) && (dqw == dqwlast);
     }
-    if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
-    tile(__builtin_amdgcn_readfirstlane((int)full) != 0, buf, n0);
+    if (!__builtin_amdgcn_readfirstlane((int)skip)) tile(__builtin_amdgcn_readfirstlane((int)full) != 0, buf, n0);
+    // the bias is loaded one tile ahead, also after a tile this wave skips,
+    // so that every processed tile finds its own bias in braw
+    if constexpr (kBias) {
+      if (n0 + BN < n_hi * BN) bias_load(n0 + BN);
+    }
   }
 
   // ---- epilogue: O / l, bf16 store (staged through LDS), optional LSE
@@ -577,6 +579,7 @@ hipError_t launch_sm(const AttnArgs& a, int sm, int mask, hipStream_t stream) {
     case SM_ALIBI: return launch_mask<D, SM_ALIBI>(a, mask, stream);
     case SM_SOFTCAP:
       return a.fixed_ref ? launch_mask<D, SM_SOFTCAP_FIXED>(a, mask, stream) : launch_mask<D, SM_SOFTCAP>(a, mask, stream);
+    case SM_TBIAS: return launch_mask<D, SM_TBIAS>(a, mask, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -76,7 +76,7 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   // Empty tensors may come with NULL data pointers: only sizes > 0 need memory.
   if ((Sq > 0 && (q == nullptr || out == nullptr)) || (Skv > 0 && (k == nullptr || v == nullptr)))
     return AV_ERR_NULL;
-  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
+  if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_BIAS) return AV_ERR_UNSUPPORTED;
   if (var->mask < AV_MASK_NONE || var->mask > AV_MASK_DOCUMENT) return AV_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;
   if (Hq % Hkv != 0) return AV_ERR_SHAPE;
@@ -84,6 +84,9 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (var->mask != AV_MASK_NONE && Sq != Skv) return AV_ERR_SHAPE;
   if (D != 32 && D != 64 && D != 128) return AV_ERR_UNSUPPORTED;
   if (var->mask == AV_MASK_DOCUMENT && var->doc_id == nullptr) return AV_ERR_NULL;
+  const bool tbias = var->score_mod == AV_SCORE_BIAS;
+  if (tbias && Sq > 0 && Skv > 0 && var->bias == nullptr) return AV_ERR_NULL;
+  if (tbias && (var->bias_batch_stride < 0 || var->bias_head_stride < 0)) return AV_ERR_PARAM;
   if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
   if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
   if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
@@ -92,11 +95,18 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
   if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
+  // bias rows are read 8 bytes at a time when Skv % 4 == 0: every slice must
+  // then start on an 8-byte boundary
+  if (tbias && (!aligned(var->bias, 8) ||
+                (Skv % 4 == 0 && (var->bias_batch_stride % 4 != 0 || var->bias_head_stride % 4 != 0))))
+    return AV_ERR_ALIGN;
   // Per-slice byte offsets are 32-bit inside the kernel; query rows of a
   // ragged last tile may index up to BM-1 rows past Sq.
   if ((uint64_t)(Sq + av::kAttnBMMax) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
   if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
-  const int bm = av::attn_bm(D, var->mask);
+  if (tbias && (uint64_t)(Sq + av::kAttnBMMax) * (Skv + 64) * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
+  const int sm = tbias ? av::SM_TBIAS : var->score_mod;
+  const int bm = av::attn_bm(D, sm, var->mask);
   const int64_t nM = ((int64_t)Sq + bm - 1) / bm;
   const int64_t total = (int64_t)B * Hq * nM;
   if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
@@ -127,7 +137,12 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   // softcapped scores lie in [-cap, cap]: with the reference at +cap every
   // exponential is in [2^(-2 cap log2 e), 1], far from fp32 underflow when <= 96
   a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
-  return hip_status(av::launch_attn_fwd(a, D, var->score_mod, var->mask, stream));
+  if (tbias) {
+    a.bias = var->bias;
+    a.bias_bs = var->bias_batch_stride;
+    a.bias_hs = var->bias_head_stride;
+  }
+  return hip_status(av::launch_attn_fwd(a, D, sm, var->mask, stream));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D) {

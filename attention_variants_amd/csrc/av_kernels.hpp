@@ -12,8 +12,12 @@ namespace av {
 // output (row-wise form); SM_GATE = no modifier, sigmoid-gate epilogue and a
 // token-major [Sq, B, Hq*D] output (column-wise form: problem b is residue
 // column b, query q is sequence q); SM_SOFTCAP_FIXED = softcap whose exponent
-// reference is fixed at the cap (chosen by the launcher when fixed_ref is set).
-enum ScoreMod : int { SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3, SM_SOFTCAP_FIXED = 4, SM_GATE = 5 };
+// reference is fixed at the cap (chosen by the launcher when fixed_ref is set);
+// SM_TBIAS = additive bias tensor read per (batch, head) through strides, the
+// plain epilogue and [B, Hq, Sq, D] output (the public AV_SCORE_BIAS).
+enum ScoreMod : int {
+  SM_NONE = 0, SM_ALIBI = 1, SM_SOFTCAP = 2, SM_BIAS = 3, SM_SOFTCAP_FIXED = 4, SM_GATE = 5, SM_TBIAS = 6
+};
 enum MaskKind : int { MK_NONE = 0, MK_CAUSAL = 1, MK_WINDOW = 2, MK_PREFIX = 3, MK_DOC = 4 };
 
 // Kernel argument block of the fused attention forward (passed by value).
@@ -24,7 +28,7 @@ struct AttnArgs {
   void* o;
   float* lse;        // nullable
   const int* doc;    // MK_DOC only
-  const void* bias;  // SM_BIAS: [Hq, Sq, Skv] bf16 pair bias, shared over the batch
+  const void* bias;  // SM_BIAS / SM_TBIAS: bf16, rows of Skv; (b, hq) slice at b * bias_bs + hq * bias_hs
   const void* gate;  // SM_BIAS: [B, Hq, Sq, D] bf16 gate pre-activations (same layout as q)
   int B, Hq, Hkv, Sq, Skv;
   int g;             // Hq / Hkv
@@ -37,6 +41,7 @@ struct AttnArgs {
   int window;
   int prefix;
   int fixed_ref;     // softcap with 2 * cap * log2(e) <= 96: exponent reference fixed at the cap
+  long long bias_bs, bias_hs;  // bias element strides of batch and head (0 = shared)
 };
 
 // Query rows per workgroup: the differential kernel uses 4 waves x 32 rows;
@@ -44,13 +49,14 @@ struct AttnArgs {
 // wave: 2 at D = 64, so every K/V fragment read from LDS feeds two MFMAs;
 // 1 at D = 128 (two blocks do not fit the register file), at D = 32 (the
 // Evoformer shapes: short rows, where more and smaller workgroups hide the
-// load latency better) and for the sliding window and document masks, whose
-// short per-row key ranges favour more, smaller workgroups.
+// load latency better), for the sliding window and document masks, whose
+// short per-row key ranges favour more, smaller workgroups, and for the bias
+// tensor (its prefetched bias tile takes the registers of a second block).
 constexpr int kAttnBM = 128;
-constexpr int attn_qb(int D, int mask) {
-  return (D == 64 && mask != MK_WINDOW && mask != MK_DOC) ? 2 : 1;
+constexpr int attn_qb(int D, int sm, int mask) {
+  return (D == 64 && mask != MK_WINDOW && mask != MK_DOC && sm != SM_TBIAS) ? 2 : 1;
 }
-constexpr int attn_bm(int D, int mask) { return 4 * 32 * attn_qb(D, mask); }
+constexpr int attn_bm(int D, int sm, int mask) { return 4 * 32 * attn_qb(D, sm, mask); }
 constexpr int kAttnBMMax = 256;
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);

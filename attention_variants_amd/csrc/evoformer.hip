@@ -205,11 +205,14 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   t.lse = nullptr;
   t.doc = nullptr;
   t.bias = a.col ? nullptr : a.bias;
+  t.bias_bs = 0;                         // the pair bias is shared by every sequence
+  t.bias_hs = (long long)L * L;
   t.B = nB;
   t.Hq = t.Hkv = a.H;
   t.Sq = t.Skv = L;
   t.g = 1;
-  t.nM = (L + attn_bm(32, MK_NONE) - 1) / attn_bm(32, MK_NONE);
+  const int bm = attn_bm(32, a.col ? SM_GATE : SM_BIAS, MK_NONE);
+  t.nM = (L + bm - 1) / bm;
   t.total = nB * a.H * t.nM;
   t.c = a.c;
   t.scale = a.c / 1.4426950408889634f;

@@ -280,6 +280,26 @@ def run_sweep(path, steps, warmup):
                       "D": 64, "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
                       "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                       "hbm_gbs": round(by / (per[0] * 1e-3) / 1e9, 1)})
+    # the bias-tensor score modifier at S = 4096: one bias per head shared over
+    # the batch ([1, 16, S, S], 537 MB) and one per (batch, head) ([4, 16, S, S], 2.1 GB)
+    S, B = 4096, 4
+    x = wi.attention_inputs(B, 16, 16, S, S, 64)
+    q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    for Bb in (1, B):
+        bias = torch.randn((Bb, 16, S, S), device=dev, generator=torch.Generator(dev).manual_seed(18),
+                           dtype=torch.float32).to(torch.bfloat16)
+        for mk in ("none", "causal"):
+            _, per = time_launches([lambda mk=mk: av.attn_fwd(q, k, v, score_mod="bias", mask=mk, bias=bias,
+                                                              out=out)], steps, warmup)
+            fl = attn_flops(B, 16, S, 64, mk)
+            by = attn_bytes(B, 16, 16, S, 64) + bias.numel() * 2 * (0.5 if mk == "causal" else 1.0)
+            tf = fl / (per[0] * 1e-3) / 1e12
+            emit({"kernel": "attn_fwd", "score_mod": "bias", "bias_shape": list(bias.shape), "mask": mk, "B": B,
+                  "Hq": 16, "Hkv": 16, "S": S, "D": 64, "us": round(per[0] * 1e3, 2),
+                  "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                  "hbm_gbs_incl_bias_once": round(by / (per[0] * 1e-3) / 1e9, 1)})
+        del bias
     for S in (1024, 4096, 16384):
         B = 16384 // S
         x = wi.diff_inputs(B, 16, S)

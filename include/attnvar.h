@@ -54,8 +54,12 @@ typedef enum {
  * supported variants").  Applied to the scaled score s = scale * q.k:
  *   AV_SCORE_ALIBI:   s + slope_h * (j - i),  slope_h = 2^(-alibi_max_bias * (h+1) / Hq)
  *                     for 0-based query head h, query row i, key row j.
- *   AV_SCORE_SOFTCAP: softcap * tanh(s / softcap). */
-typedef enum { AV_SCORE_NONE = 0, AV_SCORE_ALIBI = 1, AV_SCORE_SOFTCAP = 2 } av_score_mod;
+ *   AV_SCORE_SOFTCAP: softcap * tanh(s / softcap).
+ *   AV_SCORE_BIAS:    s + bias(b, h, i, j), read from a tensor: the
+ *                     data-dependent modifier (the talk notes' abstract sets
+ *                     Flashlight apart by data-dependent formulations; the
+ *                     Evoformer pair bias is one).  attn_fwd only. */
+typedef enum { AV_SCORE_NONE = 0, AV_SCORE_ALIBI = 1, AV_SCORE_SOFTCAP = 2, AV_SCORE_BIAS = 3 } av_score_mod;
 
 /* Masks (same section).  Key j is visible to query i when:
  *   AV_MASK_NONE:           always
@@ -86,6 +90,14 @@ typedef struct {
                              non-decreasing along each row (a precondition the host cannot
                              check: rows that break it give unspecified output) */
   int32_t kv_group;       /* Hq / Hkv (1 = MHA); 0 = derive from Hq and Hkv */
+  /* AV_SCORE_BIAS: device bf16; element (b, h, i, j) is
+   *   bias[b * bias_batch_stride + h * bias_head_stride + i * Skv + j]
+   * (strides in elements, >= 0; 0 shares one slice over every batch or
+   * query head).  8-byte aligned; when Skv % 4 == 0 both strides must be
+   * multiples of 4.  (Sq + 256) * (Skv + 64) * 2 bytes must stay below 2 GiB. */
+  const void* bias;
+  int64_t bias_batch_stride;
+  int64_t bias_head_stride;
 } av_variant;
 
 /* Fused attention forward, MHA and GQA.
@@ -113,8 +125,8 @@ int attn_fwd(const av_variant* variant, const void* q, const void* k, const void
  *   q [B, Hq, Sq, D]   k, v [B, Hkv, Skv, D]   out [B, Hq, Sq, D]
  *   lse [B, Hq, Sq] fp32, nullable (natural log, as attn_fwd)
  * Supported: D = 64; (Hq/Hkv) * Sq <= 32 (all queries of one KV head fit one
- * 32-row block); mask none or causal (causal needs Skv >= Sq); every score
- * modifier.  `workspace` (device, caller-owned, 16-byte aligned) must hold
+ * 32-row block); mask none or causal (causal needs Skv >= Sq); score
+ * modifiers none, ALiBi and softcap.  `workspace` (device, caller-owned, 16-byte aligned) must hold
  * attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) bytes; when that is 0
  * it may be NULL.  Skv == 0 writes zero rows and lse = -inf. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
@@ -156,7 +168,7 @@ int attn_decode_paged_fwd(const av_variant* variant, const void* q, const void* 
  * [B, Hkv, Skv, D], bf16 (fp32 accumulation).  `workspace` (device,
  * caller-owned, 16-byte aligned) holds attn_bwd_workspace_bytes(...) bytes.
  * Supported: D = 64; mask none or causal (causal needs Sq == Skv); every
- * score modifier.  Deterministic (no atomics). */
+ * score modifier but AV_SCORE_BIAS.  Deterministic (no atomics). */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
 int attn_bwd(const av_variant* variant, const void* q, const void* k, const void* v, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
@@ -229,7 +241,7 @@ int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, 
 const char* av_status_string(int status);
 
 /* ABI version of this header; bumped when a signature or struct changes. */
-#define AV_ABI_VERSION 1
+#define AV_ABI_VERSION 2
 int av_abi_version(void);
 
 #ifdef __cplusplus

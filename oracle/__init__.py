@@ -7,6 +7,7 @@ Every function here is pinned by ``tests/test_oracle_pins.py``.
 
 from .attention import (  # noqa: F401
     SCORE_MODS,
+    DATA_SCORE_MODS,
     MASKS,
     raw_scores,
     alibi_slope,

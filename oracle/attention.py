@@ -28,6 +28,7 @@ import math
 import numpy as np
 
 SCORE_MODS = ("none", "alibi", "softcap")
+DATA_SCORE_MODS = ("bias",)  # modifiers that read a tensor besides Q and K
 MASKS = ("none", "causal", "sliding_window", "prefix_lm", "document")
 
 
@@ -45,7 +46,10 @@ def raw_scores(q_rows: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
 # Step 2: score modifiers (talk notes, section "Evaluation: FlexAttention-
 # supported variants", which lists ALiBi and tanh soft-capping as per-element
 # score modifiers; the notes' background section describes score_mod as an
-# element-wise transform of the score).
+# element-wise transform of the score).  The additive bias tensor is the
+# data-dependent modifier: the notes' abstract sets Flashlight apart by its
+# support of data-dependent attention formulations, of which a score term read
+# from a tensor (the Evoformer's pair bias) is the plainest.
 # --------------------------------------------------------------------------
 def alibi_slope(h: int, Hq: int, max_bias: float = 8.0) -> float:
     """Slope of 0-based query head ``h``: 2^(-max_bias * (h+1) / Hq).
@@ -55,15 +59,20 @@ def alibi_slope(h: int, Hq: int, max_bias: float = 8.0) -> float:
     return 2.0 ** (-max_bias * (h + 1) / Hq)
 
 
-def apply_score_mod(s, score_mod, rows, cols, *, slope=0.0, softcap=20.0):
+def apply_score_mod(s, score_mod, rows, cols, *, slope=0.0, softcap=20.0, bias=None):
     """Element-wise score modifier on the *scaled* score.
 
     alibi:   s + slope * (j - i)        (reading: linear in signed distance,
                                          also for j > i when no mask is set)
     softcap: cap * tanh(s / cap)
+    bias:    s + bias[i, j]             (a data-dependent modifier: the value
+                                         comes from a tensor; ``bias`` holds the
+                                         rows of this (batch, head), [R, Skv])
     """
     if score_mod == "none":
         return s
+    if score_mod == "bias":
+        return s + np.asarray(bias, dtype=np.float64)
     if score_mod == "alibi":
         return s + slope * (cols[None, :].astype(np.float64) - rows[:, None].astype(np.float64))
     if score_mod == "softcap":
@@ -117,10 +126,10 @@ def softmax_two_pass(s: np.ndarray, allowed: np.ndarray):
 
 
 def _head_probs(qh, kh, rows, *, scale, score_mod, mask, slope, softcap, window, prefix_len, doc_row,
-                q_offset=0):
+                q_offset=0, bias_rows=None):
     s = raw_scores(qh[rows], kh, scale)
     pos = rows + q_offset  # absolute position of each query row
-    s = apply_score_mod(s, score_mod, pos, np.arange(kh.shape[0]), slope=slope, softcap=softcap)
+    s = apply_score_mod(s, score_mod, pos, np.arange(kh.shape[0]), slope=slope, softcap=softcap, bias=bias_rows)
     a = allowed_matrix(mask, pos, kh.shape[0], window=window, prefix_len=prefix_len, doc_row=doc_row)
     return softmax_two_pass(s, a)
 
@@ -141,8 +150,13 @@ def attention(
     rows=None,
     row_block: int = 1024,
     q_offset: int = 0,
+    bias=None,
 ):
     """out = softmax(mask(score_mod(scale * Q K^T))) V, per (batch, query head).
+
+    ``score_mod="bias"`` adds ``bias[b', h', i, j]`` (shape [Bb, Hb, Sq, Skv]
+    with Bb in {1, B} and Hb in {1, Hq}; a size-1 axis is shared by every
+    batch or head) to the scaled score before the mask.
 
     GQA reading: query head ``hq`` reads key/value head ``hq // (Hq // Hkv)``
     (contiguous groups).  ``rows`` restricts the computation to a subset of
@@ -160,8 +174,13 @@ def attention(
     B, Hq, Sq, D = q.shape
     _, Hkv, Skv, _ = k.shape
     Dv = v.shape[-1]
-    if score_mod not in SCORE_MODS:
+    if score_mod not in SCORE_MODS + DATA_SCORE_MODS:
         raise ValueError(score_mod)
+    if score_mod == "bias":
+        bias = np.asarray(bias, dtype=np.float64)
+        if bias.ndim != 4 or bias.shape[0] not in (1, B) or bias.shape[1] not in (1, Hq) \
+                or bias.shape[2:] != (Sq, Skv):
+            raise ValueError("bias must be [1 or B, 1 or Hq, Sq, Skv]")
     if mask not in MASKS:
         raise ValueError(mask)
     if Hq % Hkv:
@@ -182,11 +201,14 @@ def attention(
             slope = alibi_slope(hq, Hq, alibi_max_bias)
             for r0 in range(0, R, row_block):
                 rr = rows[r0 : r0 + row_block]
+                br = None
+                if score_mod == "bias":
+                    br = bias[b if bias.shape[0] > 1 else 0, hq if bias.shape[1] > 1 else 0][rr]
                 p, l_ = _head_probs(
                     q[b, hq], k[b, hk], rr,
                     scale=scale, score_mod=score_mod, mask=mask, slope=slope,
                     softcap=softcap, window=window, prefix_len=prefix_len, doc_row=doc_row,
-                    q_offset=q_offset,
+                    q_offset=q_offset, bias_rows=br,
                 )
                 out[b, hq, r0 : r0 + len(rr)] = p @ v[b, hk]
                 lse[b, hq, r0 : r0 + len(rr)] = l_

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.av_abi_version() == 1
+    assert lib.av_abi_version() == 2
     for code, name in av.STATUS.items():
         assert lib.av_status_string(code).decode().startswith(name)
     assert lib.av_status_string(12345).decode() == "unknown av_status"
@@ -94,6 +94,34 @@ def test_attn_fwd_rejections(lib):
     assert _attn(lib, Skv=1 << 24, D=128) == -8
     # empty query set is a no-op success
     assert _attn(lib, Sq=0, Skv=0) == 0
+
+
+def test_bias_score_mod_rejections(lib):
+    def var(bias=0x60000, bs=0, hs=128 * 128, mask="none"):
+        v = av.make_variant("bias", mask)
+        v.bias = bias
+        v.bias_batch_stride = bs
+        v.bias_head_stride = hs
+        return v
+
+    assert _attn(lib, var(bias=None)) == -1
+    assert _attn(lib, var(bias=None), Sq=0, Skv=0) == 0          # nothing to read
+    assert _attn(lib, var(bs=-4)) == -7
+    assert _attn(lib, var(hs=-1)) == -7
+    assert _attn(lib, var(bias=0x60000 + 4)) == -4              # 8-byte alignment
+    assert _attn(lib, var(hs=128 * 128 + 2)) == -4              # Skv % 4 == 0: strides multiple of 4
+    assert _attn(lib, var(hs=0), Sq=1 << 15, Skv=1 << 15) == -8  # one slice beyond 32-bit offsets
+    # Skv odd: rows are read 16 bits at a time and any stride passes the
+    # alignment check (the call still stops at the size check, before a launch)
+    assert _attn(lib, var(hs=7, bs=3), Sq=1 << 15, Skv=(1 << 15) + 1) == -8
+    bad = var()
+    bad.score_mod = 4
+    assert _attn(lib, bad) == -3
+    # the decode and backward entry points do not take the bias modifier
+    ref = ctypes.byref(var())
+    assert lib.attn_decode_fwd(ref, P, P2, P3, P4, None, 0x200000, 1 << 30, 1, 32, 8, 1, 4096, 64, None) == -3
+    assert lib.attn_bwd(ref, P, P2, P3, P4, 0x70000, P, P2, P3, 0x200000, 1 << 30, 1, 2, 2, 64, 64, 64,
+                        None) == -3
 
 
 def test_diff_attn_rejections(lib):

@@ -252,6 +252,82 @@ def test_p5_brute_force_tiny(score_mod, mask, S, D):
         np.testing.assert_allclose(lse[0, hq], np.array(bl), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- P5b: the bias tensor modifier
+@pytest.mark.parametrize("mask", oracle.MASKS)
+@pytest.mark.parametrize("bshape", ["full", "batch_shared", "head_shared", "shared"])
+def test_p5b_bias_brute_force(mask, bshape):
+    """Scalar loops with the bias element added to each scaled score."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 7, 5
+    q, k, v = _rand((B, Hq, S, D), 60), _rand((B, Hkv, S, D), 61), _rand((B, Hkv, S, 3), 62)
+    Bb = 1 if bshape in ("batch_shared", "shared") else B
+    Hb = 1 if bshape in ("head_shared", "shared") else Hq
+    bias = 2.0 * _rand((Bb, Hb, S, S), 63)
+    kw = _variant_kwargs(mask, S)
+    out, lse = oracle.attention(q, k, v, score_mod="bias", mask=mask, bias=bias, **kw)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // (Hq // Hkv)
+            bm = bias[b % Bb, hq % Hb]
+            doc = kw["doc_id"][b] if "doc_id" in kw else None
+            for i in range(S):
+                sc, ok = [], []
+                for j in range(S):
+                    x = sum(q[b, hq, i, t] * k[b, hk, j, t] for t in range(D)) / math.sqrt(D) + bm[i, j]
+                    if mask == "none":
+                        a = True
+                    elif mask == "causal":
+                        a = j <= i
+                    elif mask == "sliding_window":
+                        a = 0 <= i - j < kw["window"]
+                    elif mask == "prefix_lm":
+                        a = j < kw["prefix_len"] or j <= i
+                    else:
+                        a = doc[i] == doc[j]
+                    sc.append(x)
+                    ok.append(a)
+                mx = max(x for x, a in zip(sc, ok) if a)
+                w = [math.exp(x - mx) if a else 0.0 for x, a in zip(sc, ok)]
+                z = sum(w)
+                for e in range(3):
+                    assert out[b, hq, i, e] == pytest.approx(sum(w[j] * v[b, hk, j, e] for j in range(S)) / z,
+                                                             abs=1e-12)
+                assert lse[b, hq, i] == pytest.approx(mx + math.log(z), abs=1e-12)
+
+
+def test_p5b_bias_reductions():
+    """ALiBi written out as a tensor equals the ALiBi modifier (a transposed
+    bias flips its sign and fails); a per-row constant leaves the output and
+    shifts lse by that constant; a large bias on one key selects that key."""
+    B, H, S, D = 1, 3, 19, 8
+    q, k, v = _rand((B, H, S, D), 64), _rand((B, H, S, D), 65), _rand((B, H, S, 4), 66)
+    i = np.arange(S)[:, None]
+    j = np.arange(S)[None, :]
+    al = np.stack([oracle.alibi_slope(h, H, 8.0) * (j - i) for h in range(H)])[None].astype(np.float64)
+    for mask in ("none", "causal"):
+        o1, l1 = oracle.attention(q, k, v, score_mod="bias", mask=mask, bias=al)
+        o2, l2 = oracle.attention(q, k, v, score_mod="alibi", mask=mask)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    o3, _ = oracle.attention(q, k, v, score_mod="bias", bias=al.transpose(0, 1, 3, 2))
+    assert np.abs(o3 - o2).max() > 1e-2
+    c = 5.0 * _rand((1, 1, S, 1), 67)
+    o4, l4 = oracle.attention(q, k, v, score_mod="bias", bias=np.broadcast_to(c, (1, 1, S, S)))
+    o5, l5 = oracle.attention(q, k, v)
+    np.testing.assert_allclose(o4, o5, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l4, l5 + c[0, 0, :, 0][None, None], rtol=0, atol=1e-12)
+    onehot = np.zeros((1, 1, S, S))
+    onehot[0, 0, :, 7] = 1e3
+    o6, _ = oracle.attention(q, k, v, score_mod="bias", bias=onehot)
+    np.testing.assert_allclose(o6, np.broadcast_to(v[:, :, 7:8, :], o6.shape), rtol=0, atol=1e-12)
+
+
+def test_p5b_bias_rejects_bad_shapes():
+    q = np.zeros((2, 4, 5, 3))
+    for shape in [(3, 4, 5, 5), (2, 2, 5, 5), (2, 4, 5, 4), (4, 5, 5)]:
+        with pytest.raises(ValueError):
+            oracle.attention(q, q, q, score_mod="bias", bias=np.zeros(shape))
+
+
 # ---------------------------------------------------------------- P6
 def test_p6_gqa_equals_mha_with_repeated_kv():
     S, D = 21, 8
