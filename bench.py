@@ -458,6 +458,32 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "decode", "B": B, "Hq": Hq, "Hkv": Hkv, "Skv": Skv, "launches": steps}))
         return
+    if what == "bwd":
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        dout = _dev(wi.normal_bf16(5, (B, H, S, D), 1.0), dev)
+        out, lse = av.attn_fwd(q, k, v, return_lse=True)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(av.attn_bwd_workspace_bytes(B, H, H, S, S, D), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.attn_bwd(q, k, v, dout, lse, dq=dq, dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "bwd", "B": B, "H": H, "S": S, "D": D, "launches": steps}))
+        return
+    if what == "bias":
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        bias = _dev(wi.normal_bf16(18, (1, H, S, S), 2.0), dev)
+        out = torch.empty_like(q)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.attn_fwd(q, k, v, score_mod="bias", bias=bias, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "bias", "B": B, "H": H, "S": S, "bias": [1, H, S, S], "launches": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -490,7 +516,7 @@ def main():
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
-                                          "decode"],
+                                          "decode", "bwd", "bias"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
