@@ -232,6 +232,17 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = cap2;  // the scores hold t - m_ref already
   }
+  // Fixed-reference softcap on a tile whose raw scores all lie in
+  // |raw * scale / cap| <= 0.75: cap*tanh is an odd polynomial there
+  // (tanh(x) = x (c0 + c1 x^2 + c2 x^4 + c3 x^6) within 3.7e-6), so
+  // t - cap2 costs one multiply and four FMAs instead of exp2 + fma + rcp.
+  auto softcap_poly = [&](float raw) {
+    const float w = raw * raw;
+    float p = fmaf(w, a.sc_poly[3], a.sc_poly[2]);
+    p = fmaf(w, p, a.sc_poly[1]);
+    p = fmaf(w, p, a.sc_poly[0]);
+    return fmaf(raw, p, -cap2);
+  };
 
   i32x4 kr[NCH], vr[NCH];
   int dr = 0;
@@ -296,15 +307,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   // scores are q.k*scale + bias (natural units); the other modifiers produce log2 units
   const float cexp = kBias ? kLog2e : a.c;
 
-  // One KV tile for this wave.  Only the element mask depends on the tile
-  // class, and it edits the score registers in place, so the MFMA
-  // accumulators flow through a single path (no copies at a merge point).
-  auto tile = [&](bool full, int buf, int n0) {
-    const int kbase = n0 + 4 * hh;
-
-    // ---- S^T = K Q^T : s[qb][kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi[qb];
-    //      each K fragment read from LDS feeds the MFMAs of every query block
-    f32x16 s[QB][NKB];
+  // S^T = K Q^T of LDS tile buf for every query block
+  auto qk = [&](f32x16 (&s)[QB][NKB], int buf) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -317,12 +321,48 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(kf, qreg[qb][st_], s[qb][kb]);
       }
     }
+  };
+
+  // One KV tile for this wave.  Only the element mask depends on the tile
+  // class, and it edits the score registers in place, so the MFMA
+  // accumulators flow through a single path (no copies at a merge point).
+  auto tile = [&](bool full, int buf, int n0) {
+    const int kbase = n0 + 4 * hh;
+
+    // ---- S^T = K Q^T : s[qb][kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi[qb];
+    //      each K fragment read from LDS feeds the MFMAs of every query block
+    f32x16 s[QB][NKB];
+    qk(s, buf);
+
+    // ---- fixed-reference softcap: the polynomial form in place; a tile with
+    //      a raw score outside its range (wave-uniform, rare) recomputes
+    //      S^T from the K tile still in LDS and takes the exact exp2/rcp form
+    if constexpr (SM == SM_SOFTCAP_FIXED) {
+      float amax = 0.f;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) amax = fmaxf(amax, block_absmax<NKB>(s[qb]));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) s[qb][kb][j] = softcap_poly(s[qb][kb][j]);
+      if (any_lane(amax > a.sc_poly_lim)) {
+        qk(s, buf);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s[qb][kb][j] = softcap_t(s[qb][kb][j]);
+      }
+    }
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // ---- score modifier: ALiBi and softcap in log2 units, bias in natural
       //      units (q.k*scale + bias); vanilla keeps the raw q.k, its scale folded into exp2
-      if constexpr (SM != SM_NONE && SM != SM_GATE) {
+      if constexpr (SM != SM_NONE && SM != SM_GATE && SM != SM_SOFTCAP_FIXED) {
         // ALiBi goes straight to the exponent argument, relative to the
         // current reference: s*c + slope*(key - query) - m_sub
         float ab[4];
@@ -336,7 +376,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
           for (int j = 0; j < 16; ++j) {
             if constexpr (SM == SM_ALIBI) {
               s[qb][kb][j] = fmaf(s[qb][kb][j], a.c, ab[j & 3] + alibi_u[kb * 4 + (j >> 2)]);
-            } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+            } else if constexpr (SM == SM_SOFTCAP) {
               s[qb][kb][j] = softcap_t(s[qb][kb][j]);
             } else {  // bias: bf16 -> fp32 is a 16-bit shift
               const int wd = braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];

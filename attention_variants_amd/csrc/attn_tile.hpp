@@ -102,6 +102,23 @@ __device__ __forceinline__ float block_max(const f32x16* s) {
   return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
 }
 
+// Max of |x| over the registers of NB S^T blocks (abs is a free input
+// modifier of v_max3).
+template <int NB>
+__device__ __forceinline__ float block_absmax(const f32x16* s) {
+  float mx[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) mx[c] = fmaxf(fabsf(s[0][2 * c]), fabsf(s[0][2 * c + 1]));
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb)
+#pragma unroll
+    for (int j = (kb == 0 ? 8 : 0); j < 16; j += 2) {
+      const int c = (j >> 1) & 3;
+      mx[c] = fmaxf(fmaxf(mx[c], fabsf(s[kb][j])), fabsf(s[kb][j + 1]));
+    }
+  return fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+}
+
 // Online-softmax state of one query row held by a lane pair.  The reference
 // m_ref only has to keep the exponentials representable: the softmax is
 // exp(x - m) / sum exp(x - m) for ANY common m.

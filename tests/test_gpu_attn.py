@@ -213,3 +213,27 @@ def test_sweep_extremes(gpu_lib, S):
     rows = sample_rows(S, tiles=(128,), extra=32, seed=3)
     for sm, mk in (("softcap", "none"), ("alibi", "causal"), ("none", "document")):
         _run(gpu_lib, 16384 // S, 16, 16 if mk != "document" else 2, S, 64, sm, mk, rows=rows)
+
+
+@pytest.mark.parametrize("qmul", [0.25, 1.0, 4.0, 16.0])
+@pytest.mark.parametrize("D,mask", [(64, "none"), (64, "causal"), (32, "document"), (128, "prefix_lm")])
+def test_softcap_score_ranges(gpu_lib, qmul, D, mask):
+    """Softcap (cap 20, fixed reference) with Q scaled by a power of two: small
+    scores (every tile on the polynomial form), scores that reach past 0.75 cap
+    in some tiles (mixed forms), and scores far into saturation (exact form)."""
+    B, H, S = 2, 4, 300
+    x = wi.attention_inputs(B, H, H, S, S, D, seeds=(31, 32, 33))
+    qb = wi.bf16_bits_from_f32(wi.bf16_bits_to_f32(x["q"]) * np.float32(qmul))
+    kw = _params(mask, S)
+    if mask == "document":
+        kw["doc_id"] = wi.doc_ids(4, B, S, lo=4)
+    dev_kw = dict(kw)
+    if "doc_id" in dev_kw:
+        dev_kw["doc_id"] = torch.from_numpy(dev_kw["doc_id"]).cuda()
+    q, k, v = to_dev(qb), to_dev(x["k"]), to_dev(x["v"])
+    out, lse = gpu_lib.attn_fwd(q, k, v, score_mod="softcap", mask=mask, return_lse=True, **dev_kw)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention(f64(qb), f64(x["k"]), f64(x["v"]), score_mod="softcap", mask=mask, **kw)
+    what = f"softcap q*{qmul} D{D} {mask}"
+    assert_close(out.float().cpu().numpy(), ref, what)
+    assert_close(lse.cpu().numpy(), ref_lse, what + " lse", atol=LSE_ATOL, rtol=1e-5)
