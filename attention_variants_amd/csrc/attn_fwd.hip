@@ -233,13 +233,12 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = cap2;  // the scores hold t - m_ref already
   }
   // Fixed-reference softcap on a tile whose raw scores all lie in
-  // |raw * scale / cap| <= 0.75: cap*tanh is an odd polynomial there
-  // (tanh(x) = x (c0 + c1 x^2 + c2 x^4 + c3 x^6) within 3.7e-6), so
-  // t - cap2 costs one multiply and four FMAs instead of exp2 + fma + rcp.
+  // |raw * scale / cap| <= 0.5: cap*tanh is an odd polynomial there
+  // (tanh(x) = x (c0 + c1 x^2 + c2 x^4) within 5.3e-6), so t - cap2 costs
+  // one multiply and three FMAs instead of exp2 + fma + rcp.
   auto softcap_poly = [&](float raw) {
     const float w = raw * raw;
-    float p = fmaf(w, a.sc_poly[3], a.sc_poly[2]);
-    p = fmaf(w, p, a.sc_poly[1]);
+    float p = fmaf(w, a.sc_poly[2], a.sc_poly[1]);
     p = fmaf(w, p, a.sc_poly[0]);
     return fmaf(raw, p, -cap2);
   };
@@ -487,13 +486,20 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
 
     // ---- O^T += V^T P^T; each transposed V fragment feeds every query block
+    // all V^T operands of the tile are read before the first MFMA (the
+    // scheduler would otherwise keep two in flight and wait on LDS eight times)
+    bf16x8 vfa[NDB][NPS];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < NPS; ++t) vfa[db][t] = vt_operand<D>(Vs[buf], t, db * 32, vl);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int t = 0; t < NPS; ++t) {
-        const bf16x8 vf = vt_operand<D>(Vs[buf], t, db * 32, vl);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vf, pb[qb][t], o[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(vfa[db][t], pb[qb][t], o[qb][db]);
       }
   };
 
