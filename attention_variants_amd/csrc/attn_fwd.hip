@@ -588,12 +588,18 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
   }
   if constexpr (kStageQO) {
-    // O tile: rows q0 .. q0+BM-1 of the (b, hq) slice, contiguous in memory
+    // O tile: rows q0 .. q0+BM-1 of the (b, hq) slice, contiguous in memory.
+    // The offsets are those of the Q tile load; with a score modifier, an
+    // opaque copy of the thread id keeps the compiler from computing them
+    // once before the key loop and spilling them across it (vanilla has the
+    // registers to hold them, and runs faster with its own schedule).
     __syncthreads();
     bf16* obase = (bf16*)a.o + qoff;
+    int tid_e = tid;
+    if constexpr (SM != SM_NONE) asm volatile("" : "+v"(tid_e));
 #pragma unroll
     for (int c = 0; c < QCH; ++c) {
-      const int idx = tid + NT * c;
+      const int idx = tid_e + NT * c;
       const int row = idx / CPR, col = idx % CPR;
       if (q0 + row < a.Sq) *(i32x4*)(obase + (size_t)(q0 + row) * D + col * 8) = *(const i32x4*)&QOs[row * KP + col * 8];
     }

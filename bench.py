@@ -79,9 +79,9 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+def measured_traffic(score_mod="none"):
+    """HBM bytes per launch of the kernel of `score_mod` from the committed
+    counter summary, if it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "attn_fwd_S4096_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -93,7 +93,7 @@ def measured_traffic():
     if kv.get("kernel_source_sha") != kernel_source_sha():
         return None
     try:
-        return float(kv["traffic_bytes_per_launch"])
+        return float(kv[f"traffic_bytes_per_launch.{score_mod}"])
     except (KeyError, ValueError):
         return None
 
@@ -202,7 +202,7 @@ def run_headline(args):
         variants[sm] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     dom = max(range(3), key=lambda i: per_ms[i])
     achieved = fl / (per_ms[dom] * 1e-3) / 1e12
-    traffic = measured_traffic()
+    traffic = measured_traffic(mods[dom])
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
