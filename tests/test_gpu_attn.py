@@ -15,7 +15,8 @@ import torch
 import oracle
 from workloads import inputs as wi
 
-from .gpu_util import assert_close, canary_empty, canary_intact, f64, sample_rows, to_dev
+from .gpu_util import (assert_close, assert_rms_rel, canary_empty, canary_intact, f64, sample_rows,
+                       sample_rows_at_least, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,9 @@ def _params(mask, S, seed_doc=4, doc_lo=64):
 
 
 def _run(av, B, Hq, Hkv, S, D, score_mod, mask, rows=None, seed=(1, 2, 3), Skv=None, check_lse=True,
-         canary=True, softcap=20.0):
+         canary=True, softcap=20.0, batch=None, rms_check=False):
+    """GPU on the whole shape; the oracle on `rows` (default all) of every
+    batch entry, or of batch entry `batch` only (batch entries are independent)."""
     Skv = S if Skv is None else Skv
     x = wi.attention_inputs(B, Hq, Hkv, S, Skv, D, seeds=seed)
     kw = _params(mask, S)
@@ -54,16 +57,23 @@ def _run(av, B, Hq, Hkv, S, D, score_mod, mask, rows=None, seed=(1, 2, 3), Skv=N
     if canary:
         assert canary_intact(big, out.numel()), "write past the end of out"
         assert canary_intact(bigl, lse.numel()), "write past the end of lse"
-    ref, ref_lse = oracle.attention(f64(x["q"]), f64(x["k"]), f64(x["v"]), score_mod=score_mod, mask=mask,
-                                    softcap=softcap, rows=rows, **kw)
     got = out.float().cpu().numpy()
     got_lse = lse.cpu().numpy()
+    bs = slice(None) if batch is None else slice(batch, batch + 1)
+    okw = dict(kw)
+    if "doc_id" in okw:
+        okw["doc_id"] = okw["doc_id"][bs]
+    ref, ref_lse = oracle.attention(f64(x["q"][bs]), f64(x["k"][bs]), f64(x["v"][bs]), score_mod=score_mod,
+                                    mask=mask, softcap=softcap, rows=rows, **okw)
+    got, got_lse = got[bs], got_lse[bs]
     if rows is not None:
         got, got_lse = got[:, :, rows], got_lse[:, :, rows]
     what = f"{score_mod}/{mask} B{B} Hq{Hq} Hkv{Hkv} S{S} Skv{Skv} D{D}"
     err = assert_close(got, ref, what)
     if check_lse:
         assert_close(got_lse, ref_lse, what + " lse", atol=LSE_ATOL, rtol=1e-5)
+    if rms_check:
+        assert_rms_rel(got, ref, what)
     return err, out
 
 
@@ -188,11 +198,24 @@ def test_deterministic(gpu_lib):
 
 
 # ------------------------------------------------------------- benchmark shapes
+BENCH_VARIANTS = ([(sm, "none", 16) for sm in SCORE_MODS]
+                  + [("none", mk, hkv) for mk in MASKS[1:] for hkv in (16, 2)])
+
+
+@pytest.mark.parametrize("S", [512, 1024, 2048])
+@pytest.mark.parametrize("score_mod,mask,Hkv", BENCH_VARIANTS)
+def test_benchmark_shapes_all_rows(gpu_lib, S, score_mod, mask, Hkv):
+    """The benchmark shapes up to S = 2k (16k tokens, 16 query heads): every
+    row of every head, for the last batch entry (entries are independent)."""
+    B = 16384 // S
+    _run(gpu_lib, B, 16, Hkv, S, 64, score_mod, mask, batch=B - 1, rms_check=True)
+
+
 @pytest.mark.parametrize("score_mod", SCORE_MODS)
 def test_score_mod_sweep_S4096(gpu_lib, score_mod):
     S = 4096
-    rows = sample_rows(S, extra=64, seed=1)
-    _run(gpu_lib, 16384 // S, 16, 16, S, 64, score_mod, "none", rows=rows)
+    rows = sample_rows_at_least(S, 512, seed=1)
+    _run(gpu_lib, 16384 // S, 16, 16, S, 64, score_mod, "none", rows=rows, rms_check=True)
 
 
 @pytest.mark.parametrize("mask", MASKS[1:])
@@ -204,15 +227,24 @@ def test_mask_sweep_S4096(gpu_lib, mask, Hkv):
     if mask == "document":
         for b_lens in wi.doc_lengths(4, B, S):
             must += list(np.cumsum(b_lens)[:-1]) + list(np.cumsum(b_lens)[:-1] - 1)
-    rows = sample_rows(S, extra=48, seed=2, must=must)
-    _run(gpu_lib, B, 16, Hkv, S, 64, "none", mask, rows=rows)
+    rows = sample_rows_at_least(S, 512, seed=2, must=must)
+    _run(gpu_lib, B, 16, Hkv, S, 64, "none", mask, rows=rows, rms_check=True)
 
 
 @pytest.mark.parametrize("S", [512, 16384])
 def test_sweep_extremes(gpu_lib, S):
-    rows = sample_rows(S, tiles=(128,), extra=32, seed=3)
+    rows = sample_rows_at_least(S, 512, tiles=(128,), seed=3)
     for sm, mk in (("softcap", "none"), ("alibi", "causal"), ("none", "document")):
-        _run(gpu_lib, 16384 // S, 16, 16 if mk != "document" else 2, S, 64, sm, mk, rows=rows)
+        _run(gpu_lib, 16384 // S, 16, 16 if mk != "document" else 2, S, 64, sm, mk, rows=rows, rms_check=True)
+
+
+@pytest.mark.parametrize("score_mod", SCORE_MODS)
+def test_score_mod_S16384_rms(gpu_lib, score_mod):
+    """S = 16k, where outputs have rms ~ 0.013: at least 512 rows per head,
+    elementwise gate plus the rms-relative diagnostic."""
+    S = 16384
+    rows = sample_rows_at_least(S, 512, tiles=(128,), seed=4)
+    _run(gpu_lib, 1, 16, 16, S, 64, score_mod, "none", rows=rows, rms_check=True)
 
 
 @pytest.mark.parametrize("qmul", [0.25, 1.0, 4.0, 16.0])
