@@ -446,8 +446,8 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "evoformer_col", "Ns": Ns, "Nr": Nr, "launches": steps}))
         return
-    if what == "decode":
-        B, Hq, Hkv, Skv, D = 64, 32, 8, 4096, 64
+    if what in ("decode", "decode_b1"):
+        B, Hq, Hkv, Skv, D = (64, 32, 8, 4096, 64) if what == "decode" else (1, 32, 8, 16384, 64)
         x = wi.attention_inputs(B, Hq, Hkv, 1, Skv, D)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
         out = torch.empty_like(q)
@@ -456,7 +456,7 @@ def run_profile(what, steps, nres=256):
         for _ in range(steps):
             av.attn_decode_fwd(q, k, v, score_mod="softcap", mask="causal", out=out, workspace=ws)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": "decode", "B": B, "Hq": Hq, "Hkv": Hkv, "Skv": Skv, "launches": steps}))
+        print(json.dumps({"profile": what, "B": B, "Hq": Hq, "Hkv": Hkv, "Skv": Skv, "launches": steps}))
         return
     if what == "bwd":
         B, H, S, D = 4, 16, 4096, 64
@@ -516,7 +516,7 @@ def main():
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
-                                          "decode", "bwd", "bias"],
+                                          "decode", "decode_b1", "bwd", "bias"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
