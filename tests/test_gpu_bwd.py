@@ -56,3 +56,24 @@ def test_bwd_deterministic(gpu_lib):
     r = [gpu_lib.attn_bwd(q, k, v, dout, lse, mask="causal") for _ in range(3)]
     for i in range(3):
         assert torch.equal(r[0][i], r[1][i]) and torch.equal(r[1][i], r[2][i])
+
+
+@pytest.mark.parametrize("score_mod,mask", [("none", "none"), ("softcap", "causal")])
+def test_bwd_benchmark_shape(gpu_lib, score_mod, mask):
+    """The benchmark shape (B = 4, H = 16, S = 4096): the GPU computes every
+    head; the oracle checks the first two heads of the last batch entry (heads
+    and batch entries are independent for these score modifiers)."""
+    B, H, S, D = 4, 16, 4096, 64
+    x = wi.attention_inputs(B, H, H, S, S, D)
+    g = wi.normal_bf16(5, (B, H, S, D), 1.0)
+    q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    kw = dict(score_mod=score_mod, mask=mask, softcap=20.0)
+    out, lse = gpu_lib.attn_fwd(q, k, v, return_lse=True, **kw)
+    dq, dk, dv = gpu_lib.attn_bwd(q, k, v, dout, lse, **kw)
+    torch.cuda.synchronize()
+    sl = (slice(B - 1, B), slice(0, 2))
+    rq, rk, rv = oracle.attention_backward(f64(x["q"][sl]), f64(x["k"][sl]), f64(x["v"][sl]), f64(g[sl]), **kw)
+    what = f"bwd {score_mod}/{mask} B{B} H{H} S{S} (batch {B - 1}, heads 0-1)"
+    assert_close(dq[sl].float().cpu().numpy(), rq, what + " dq")
+    assert_close(dk[sl].float().cpu().numpy(), rk, what + " dk")
+    assert_close(dv[sl].float().cpu().numpy(), rv, what + " dv")
