@@ -31,15 +31,36 @@
 namespace av {
 namespace {
 
-constexpr int GM = 128;  // tokens per workgroup
-constexpr int GN = 128;  // output channels per workgroup
 constexpr int GK = 64;   // K chunk staged in LDS
-constexpr int NT = 256;
 constexpr int MP = GK + 8;   // m tile pitch: 8 rows -> 8 distinct 16-byte bank groups
 
-__global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 Ms[2][GM * MP];
-  __shared__ __attribute__((aligned(16))) bf16 Ws[2][GK * GN];  // swizzled for transposed reads
+// Row-major W tile of GN (128 or 256) columns read by transposed LDS reads: a
+// read serves 4 consecutive rows x 64 bytes, which must fall in distinct
+// 64-byte segments of the 256-byte bank window, so the 64-byte segments of
+// row r are XOR-permuted by r mod 4.
+__device__ __forceinline__ int w_swz(int row) { return row & 3; }
+template <int GN>
+__device__ __forceinline__ int w_off(int row, int c) { return row * GN + (c ^ (w_swz(row) << 5)); }
+
+// GM tokens x GN channels per workgroup of NT threads; each wave computes 64
+// channels x (GM / WM) tokens.  The 256 x 256 form (8 waves) reads half the
+// operand bytes per FLOP of the 128 x 128 form (with K = Cm = 256 the MFMAs
+// are a small part of the time) but holds one workgroup per CU.
+template <int GM, int GN, int NT>
+__global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const EvoArgs a) {
+  constexpr int NW = NT / 64;
+  constexpr int WN = GN / 64;            // waves along the channels
+  constexpr int WM = NW / WN;            // waves along the tokens
+  constexpr int MB = GM / WM / 32;       // 32-token MFMA blocks per wave
+  constexpr int MCH = GM * GK / 8 / NT;  // 16-byte m chunks per thread and K chunk
+  constexpr int WCH = GK * GN / 8 / NT;  // 16-byte W chunks per thread and K chunk
+  static_assert(WN * WM == NW && MB >= 1 && MCH >= 1 && WCH >= 1, "tile/thread mismatch");
+  constexpr int M_ELEMS = GM * MP, W_ELEMS = GK * GN;
+  constexpr int CP = GN + 8;             // epilogue C tile pitch
+  constexpr int LDS_ELEMS = 2 * (M_ELEMS + W_ELEMS) > GM * CP ? 2 * (M_ELEMS + W_ELEMS) : GM * CP;
+  __shared__ __attribute__((aligned(16))) bf16 lds[LDS_ELEMS];
+  bf16* const Ms0 = lds;
+  bf16* const Ws0 = lds + 2 * M_ELEMS;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -53,7 +74,7 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
   const int n0 = nt * GN;
   const int p = n0 / HD;                       // projection of this tile (GN divides HD)
   const int c0 = n0 % HD;
-  const int wn = w & 1, wm = w >> 1;           // wave: 64 channels x 64 tokens
+  const int wn = w % WN, wm = w / WN;          // wave: 64 channels x GM / WM tokens
 
   // Token order: row-wise, token t = (sequence, residue) in MSA order; column-
   // wise, t = residue * Ns + sequence, so that the tokens of one attention
@@ -67,32 +88,38 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
 
   // byte offset of the m row of each token this thread stages (past the end:
   // tokens beyond M, read as zeros)
-  uint32_t mrow_off[4];
+  uint32_t mrow_off[MCH];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < MCH; ++c) {
     const int t = mt * GM + ((tid + NT * c) >> 3);
     const int row = a.col ? (t % a.Ns) * a.Nr + t / a.Ns : t;
     mrow_off[c] = t < M ? (uint32_t)row * a.Cm * 2 : m_bytes;
   }
 
-  // staging: m chunk 128 x 64 and W chunk 64 x 128, 4 x 16 bytes per thread each
-  i32x4 mr[4], wr[4];
+  i32x4 mr[MCH], wr[WCH];
   auto gload = [&](int kc) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < MCH; ++c) {
       const int idx = tid + NT * c;
-      const int mcol = idx & 7;
-      mr[c] = buf_load16(mrs, mrow_off[c] + (uint32_t)(kc * GK + mcol * 8) * 2);
-      const int wrow = idx >> 4, wcol = idx & 15;
+      mr[c] = buf_load16(mrs, mrow_off[c] + (uint32_t)(kc * GK + (idx & 7) * 8) * 2);
+    }
+#pragma unroll
+    for (int c = 0; c < WCH; ++c) {
+      const int idx = tid + NT * c;
+      const int wrow = idx / (GN / 8), wcol = idx % (GN / 8);
       wr[c] = buf_load16(wrs, (uint32_t)((kc * GK + wrow) * HD + c0 + wcol * 8) * 2);
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < MCH; ++c) {
       const int idx = tid + NT * c;
-      *(i32x4*)&Ms[buf][(idx >> 3) * MP + (idx & 7) * 8] = mr[c];
-      *(i32x4*)&Ws[buf][tr_tile_off<GN>(idx >> 4, (idx & 15) * 8)] = wr[c];
+      *(i32x4*)&Ms0[buf * M_ELEMS + (idx >> 3) * MP + (idx & 7) * 8] = mr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < WCH; ++c) {
+      const int idx = tid + NT * c;
+      *(i32x4*)&Ws0[buf * W_ELEMS + w_off<GN>(idx / (GN / 8), (idx % (GN / 8)) * 8)] = wr[c];
     }
   };
 
@@ -101,11 +128,13 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
   // Those rows are congruent to r/4 mod 4, so the tile swizzle is a per-lane constant.
   const int wr_row = 8 * hh + ((lane & 15) >> 2);
   const int wr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int wr_xo = tr_swz<GN>((lane & 15) >> 2) << 5;
+  const int wr_xo = w_swz((lane & 15) >> 2) << 5;
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][MB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x16{};
 
   const int nkc = a.Cm / GK;
   gload(0);
@@ -114,38 +143,39 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
     sstore(buf);
     __syncthreads();
     if (kc + 1 < nkc) gload(kc + 1);
+    const bf16* Ms = Ms0 + buf * M_ELEMS;
+    const bf16* Ws = Ws0 + buf * W_ELEMS;
 #pragma unroll
     for (int ks = 0; ks < GK / 16; ++ks) {
-      bf16x8 wa[2], mb[2];
+      bf16x8 wa[2], mb[MB];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const bf16* wp = &Ws[buf][(ks * 16 + wr_row) * GN + ((wn * 64 + nb * 32 + wr_col) ^ wr_xo)];
+        const bf16* wp = &Ws[(ks * 16 + wr_row) * GN + ((wn * 64 + nb * 32 + wr_col) ^ wr_xo)];
         const i16x4 lo = lds_read_tr16(wp);
         const i16x4 hi = lds_read_tr16(wp + 4 * GN);
         wa[nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
-      for (int mb2 = 0; mb2 < 2; ++mb2) mb[mb2] = *(const bf16x8*)&Ms[buf][(wm * 64 + mb2 * 32 + l32) * MP + ks * 16 + hh * 8];
+      for (int mb2 = 0; mb2 < MB; ++mb2)
+        mb[mb2] = *(const bf16x8*)&Ms[(wm * MB * 32 + mb2 * 32 + l32) * MP + ks * 16 + hh * 8];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb2 = 0; mb2 < 2; ++mb2) acc[nb][mb2] = mfma32(wa[nb], mb[mb2], acc[nb][mb2]);
+        for (int mb2 = 0; mb2 < MB; ++mb2) acc[nb][mb2] = mfma32(wa[nb], mb[mb2], acc[nb][mb2]);
     }
   }
 
-  // Epilogue through LDS: the 128 x 128 bf16 C tile is staged token-major
-  // (row pitch CP keeps rows 16-byte aligned; the 32 tokens of one 8-byte
-  // write spread over the banks with at most 2-way conflicts), then written
-  // out as 16-byte chunks.  In the head-major planes the 32
-  // channels of one head are 64 contiguous bytes per token, so consecutive
-  // tokens of one head form one contiguous run.
-  constexpr int CP = GN + 8;
-  static_assert(GM * CP * 2 <= (int)sizeof(Ms), "C tile does not fit the m staging buffers");
-  __syncthreads();  // every wave is done with Ms / Ws
-  bf16* Cs = &Ms[0][0];
+  // Epilogue through LDS: the GM x GN bf16 C tile is staged token-major (row
+  // pitch CP keeps rows 16-byte aligned; the 32 tokens of one 8-byte write
+  // spread over the banks with at most 2-way conflicts), then written out as
+  // 16-byte chunks.  In the head-major planes the 32 channels of one head are
+  // 64 contiguous bytes per token, so consecutive tokens of one head form one
+  // contiguous run.
+  __syncthreads();  // every wave is done with the staging tiles
+  bf16* Cs = lds;
 #pragma unroll
-  for (int mb2 = 0; mb2 < 2; ++mb2) {
-    const int tl = wm * 64 + mb2 * 32 + l32;
+  for (int mb2 = 0; mb2 < MB; ++mb2) {
+    const int tl = wm * MB * 32 + mb2 * 32 + l32;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
@@ -184,9 +214,16 @@ __global__ __launch_bounds__(NT, 2) void evo_proj_kernel(const EvoArgs a) {
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
 
 hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
-  const int M = a.Ns * a.Nr, N = 4 * a.H * a.dh;
-  const int gemm_blocks = ((M + GM - 1) / GM) * (N / GN);
-  hipLaunchKernelGGL(evo_proj_kernel, dim3(gemm_blocks), dim3(NT), 0, stream, a);
+  const int M = a.Ns * a.Nr, HD = a.H * a.dh, N = 4 * HD;
+  // The 256 x 256 tile (one workgroup per CU) pays once its grid fills the
+  // 256 CUs at least four times over (N_res = 768 at 128 sequences: -5 %);
+  // smaller grids keep the 128 x 128 tile at two workgroups per CU.
+  const long long big_tiles = (long long)((M + 255) / 256) * (N / 256);
+  if (HD % 256 == 0 && big_tiles >= 4 * 256) {
+    hipLaunchKernelGGL((evo_proj_kernel<256, 256, 512>), dim3(((M + 255) / 256) * (N / 256)), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((evo_proj_kernel<128, 128, 256>), dim3(((M + 127) / 128) * (N / 128)), dim3(256), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
