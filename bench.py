@@ -522,8 +522,8 @@ def main():
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 (no multi-GPU path exists)",
-              file=sys.stderr)
+        print("bench.py: measures one GPU only; --gpus must be 1 (the library has no multi-GPU path; "
+              "sharding is a design note, not code)", file=sys.stderr)
         sys.exit(2)
     if args.sweep:
         run_sweep(args.sweep, args.steps, args.warmup)
