@@ -70,9 +70,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int nKT = (a.Skv + 127) / 128;
-  const int L = xcd_remap(blockIdx.x, a.total);
-  const int kt = L % nKT;
-  const int bk = L / nKT;
+  int kt, bk;
+  if constexpr (CAUSAL) {  // key tile 0 is reached by every query: heaviest first
+    const TileIdx ti = weighted_tile(blockIdx.x, a.total, nKT);
+    kt = ti.mt_lin;
+    bk = ti.bh;
+  } else {
+    const int L = xcd_remap(blockIdx.x, a.total);
+    kt = L % nKT;
+    bk = L / nKT;
+  }
   const int hk = bk % a.Hkv, b = bk / a.Hkv;
   const int k0 = kt * 128;
   const int kw0 = k0 + 32 * w;      // first key of this wave
@@ -236,9 +243,16 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int nM = (a.Sq + 127) / 128;
-  const int L = xcd_remap(blockIdx.x, a.total_q);
-  const int mt_lin = L % nM;
-  const int bh = L / nM;
+  int mt_lin, bh;
+  if constexpr (CAUSAL) {
+    const TileIdx ti = weighted_tile(blockIdx.x, a.total_q, nM);
+    mt_lin = ti.mt_lin;
+    bh = ti.bh;
+  } else {
+    const int L = xcd_remap(blockIdx.x, a.total_q);
+    mt_lin = L % nM;
+    bh = L / nM;
+  }
   const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / a.g;
   const int mt = CAUSAL ? nM - 1 - mt_lin : mt_lin;  // heaviest query tiles first

@@ -97,9 +97,16 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   const int hh = lane >> 5, l32 = lane & 31;
 
   // ---- logical tile of this workgroup
-  const int L = xcd_remap(blockIdx.x, a.total);
-  const int mt_lin = L % a.nM;
-  const int bh = L / a.nM;
+  int mt_lin, bh;
+  if constexpr (MK == MK_CAUSAL || MK == MK_PREFIX) {
+    const TileIdx ti = weighted_tile(blockIdx.x, a.total, a.nM);
+    mt_lin = ti.mt_lin;
+    bh = ti.bh;
+  } else {
+    const int L = xcd_remap(blockIdx.x, a.total);
+    mt_lin = L % a.nM;
+    bh = L / a.nM;
+  }
   // Evoformer (pair bias shared over the batch): heads outermost, so one XCD's
   // run of tiles covers few heads and their bias stays in its L2.
   const int hq = (SM == SM_BIAS) ? bh / a.B : bh % a.Hq;

@@ -93,6 +93,26 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   return x * q + (x < r ? x : r) + i;
 }
 
+// Logical tile of workgroup pid for grids whose query tiles differ in cost
+// (causal and PrefixLM masks; mt_lin = 0 is the heaviest tile of a head).
+// When the (batch, head) count is a multiple of 8, XCD x owns heads
+// [x*G, (x+1)*G) as under xcd_remap, but receives their tiles heaviest first
+// across all G heads: its CUs then take work in longest-first order, where
+// head after head (heavy to light within each) leaves a long tail of heavy
+// tiles that start late.  Otherwise the order of xcd_remap.
+struct TileIdx {
+  int bh, mt_lin;
+};
+__device__ __forceinline__ TileIdx weighted_tile(int pid, int total, int nM) {
+  const int BH = total / nM;
+  if ((BH & 7) == 0) {
+    const int G = BH >> 3, x = pid & 7, i = pid >> 3;
+    return {x * G + i % G, i / G};
+  }
+  const int L = xcd_remap(pid, total);
+  return {L / nM, L % nM};
+}
+
 // First index in [0, n) whose value exceeds `target` in a non-decreasing
 // int row (n when none).  All 64 lanes of the wave cooperate: each round
 // probes 64 evenly spaced positions and keeps the gap where the predicate

@@ -54,9 +54,16 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
 
-  const int L = xcd_remap(blockIdx.x, a.total);
-  const int mt_lin = L % a.nM;
-  const int bh = L / a.nM;
+  int mt_lin, bh;
+  if (a.causal) {
+    const TileIdx ti = weighted_tile(blockIdx.x, a.total, a.nM);
+    mt_lin = ti.mt_lin;
+    bh = ti.bh;
+  } else {
+    const int L = xcd_remap(blockIdx.x, a.total);
+    mt_lin = L % a.nM;
+    bh = L / a.nM;
+  }
   const int mt = a.causal ? (a.nM - 1 - mt_lin) : mt_lin;
   const int S = a.S;
   const int q0 = mt * BM;
