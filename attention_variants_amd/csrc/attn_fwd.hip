@@ -510,16 +510,25 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       }
   };
 
-  if (n_lo < n_hi) gload(n_lo);
+  // Key tile order.  ALiBi walks the keys from last to first: its term grows
+  // with the key index (by up to ~65 log2 units per tile on the steepest
+  // heads), so in ascending order most tiles would raise the exponent
+  // reference and rescale O; descending, the first tile holds the row's
+  // largest term and later tiles rarely raise it.
+  constexpr bool kDescending = SM == SM_ALIBI;
+  auto tile_at = [&](int it) { return kDescending ? n_hi - 1 - (it - n_lo) : it; };
+
+  if (n_lo < n_hi) gload(tile_at(n_lo));
   if constexpr (kBias) {
-    if (n_lo < n_hi) bias_load(n_lo * BN);
+    if (n_lo < n_hi) bias_load(tile_at(n_lo) * BN);
   }
 
-  for (int nt = n_lo; nt < n_hi; ++nt) {
-    const int buf = (nt - n_lo) & 1;
+  for (int it = n_lo; it < n_hi; ++it) {
+    const int nt = tile_at(it);
+    const int buf = (it - n_lo) & 1;
     sstore(buf);
     __syncthreads();
-    if (nt + 1 < n_hi) gload(nt + 1);
+    if (it + 1 < n_hi) gload(tile_at(it + 1));
 
     const int n0 = nt * BN, n1 = n0 + BN - 1;
     // ---- per-wave tile class: skip / full / partial (wave-uniform)
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     // the bias is loaded one tile ahead, also after a tile this wave skips,
     // so that every processed tile finds its own bias in braw
     if constexpr (kBias) {
-      if (n0 + BN < n_hi * BN) bias_load(n0 + BN);
+      if (it + 1 < n_hi) bias_load(tile_at(it + 1) * BN);
     }
   }
 
