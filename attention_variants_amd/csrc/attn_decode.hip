@@ -119,7 +119,10 @@ __global__ __launch_bounds__(NT, (PAGED ? 2 : 3)) void attn_decode_kernel(const 
   // per-row ALiBi slope (log2 units); rows of one workgroup span several heads
   const float slope2 = SM == SM_ALIBI ? kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq) : 0.f;
 
-  for (int t = t_lo + w; t < t_hi; t += 4) {
+  // ALiBi walks the split's tiles from last to first (its term grows with the
+  // key index; descending, later tiles seldom raise the exponent reference)
+  for (int i = w; i < t_hi - t_lo; i += 4) {
+    const int t = SM == SM_ALIBI ? t_hi - 1 - i : t_lo + i;
     const int n0 = t * BN;
     const int pg = tile_page(n0);
     // ---- V tile -> registers -> this wave's LDS slot (row-major, swizzled)
