@@ -34,6 +34,8 @@ STATUS = {
 # Names the header declares; tests check that the library exports each one.
 EXPORTED = (
     "attn_fwd",
+    "attn_doc_order_len",
+    "attn_doc_order",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
     "attn_decode_paged_workspace_bytes",
@@ -66,6 +68,7 @@ class AvVariant(ctypes.Structure):
         ("bias", ctypes.c_void_p),
         ("bias_batch_stride", ctypes.c_int64),
         ("bias_head_stride", ctypes.c_int64),
+        ("doc_order", ctypes.c_void_p),
     ]
 
 
@@ -87,6 +90,10 @@ def load_library(path: str | None = None):
     lib = ctypes.CDLL(p)
     lib.attn_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_fwd.restype = _i
+    lib.attn_doc_order_len.argtypes = [_i, _i]
+    lib.attn_doc_order_len.restype = _i
+    lib.attn_doc_order.argtypes = [_vp, _i, _i, _vp, _i, _vp]
+    lib.attn_doc_order.restype = _i
     lib.attn_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i]
     lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
@@ -156,7 +163,7 @@ def _need(t, name, dtype, ndim):
 
 def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alibi_max_bias=8.0,
                  window=256, prefix_len=0, doc_id=None, kv_group=0, bias=None, bias_batch_stride=0,
-                 bias_head_stride=0) -> AvVariant:
+                 bias_head_stride=0, doc_order=None) -> AvVariant:
     if score_mod not in SCORE_MODS:
         raise ValueError(f"unknown score_mod {score_mod!r}")
     if mask not in MASKS:
@@ -164,15 +171,18 @@ def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alib
     return AvVariant(SCORE_MODS[score_mod], MASKS[mask], float(scale or 0.0), float(softcap),
                      float(alibi_max_bias), int(window), int(prefix_len),
                      None if doc_id is None else int(doc_id.data_ptr()), int(kv_group),
-                     None if bias is None else int(bias.data_ptr()), int(bias_batch_stride), int(bias_head_stride))
+                     None if bias is None else int(bias.data_ptr()), int(bias_batch_stride), int(bias_head_stride),
+                     None if doc_order is None else int(doc_order.data_ptr()))
 
 
 def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0, alibi_max_bias=8.0,
-             window=256, prefix_len=0, doc_id=None, kv_group=0, bias=None, return_lse=False, out=None, lse=None):
+             window=256, prefix_len=0, doc_id=None, kv_group=0, bias=None, return_lse=False, out=None, lse=None,
+             doc_order=None):
     """Fused attention forward.  q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] bf16 -> out [B,Hq,Sq,D] (bf16).
 
     ``score_mod="bias"`` adds ``bias`` (bf16 [Bb, Hb, Sq, Skv], Bb in {1, B},
     Hb in {1, Hq}; a size-1 axis is shared) to the scaled scores.
+    ``doc_order`` (document mask only): the work order ``attn_doc_order(doc_id)`` returns.
     With ``return_lse`` also returns the fp32 natural-log sum-exp per row.
     """
     import torch
@@ -188,6 +198,10 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
         _need(doc_id, "doc_id", torch.int32, 2)
         if tuple(doc_id.shape) != (B, Sq):
             raise ValueError("doc_id must be [B, S]")
+    if doc_order is not None:
+        _need(doc_order, "doc_order", torch.int32, 1)
+        if doc_order.numel() != attn_doc_order_len(B, Sq):
+            raise ValueError("doc_order must come from attn_doc_order(doc_id) of this shape")
     bs = hs = 0
     if score_mod == "bias":
         if bias is None:
@@ -208,11 +222,35 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
                        window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group, bias=bias,
-                       bias_batch_stride=bs, bias_head_stride=hs)
+                       bias_batch_stride=bs, bias_head_stride=hs, doc_order=doc_order)
     rc = lib.attn_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                       None if lse is None else lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
     _check(rc, "attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_doc_order_len(B, S) -> int:
+    n = int(load_library().attn_doc_order_len(B, S))
+    _check(min(n, 0), "attn_doc_order_len")
+    return n
+
+
+def attn_doc_order(doc_id, out=None):
+    """Heaviest-first work order of attn_fwd's query tiles under the document
+    mask, from ``doc_id`` [B, S] int32: an int32 tensor of attn_doc_order_len(B, S)."""
+    import torch
+
+    lib = load_library()
+    _need(doc_id, "doc_id", torch.int32, 2)
+    B, S = doc_id.shape
+    n = attn_doc_order_len(B, S)
+    if out is None:
+        out = torch.empty((n,), dtype=torch.int32, device=doc_id.device)
+    else:
+        _need(out, "out", torch.int32, 1)
+    rc = lib.attn_doc_order(doc_id.data_ptr(), B, S, out.data_ptr(), out.numel(), _stream_ptr(doc_id.device))
+    _check(rc, "attn_doc_order")
+    return out
 
 
 def attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) -> int:

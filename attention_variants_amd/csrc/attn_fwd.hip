@@ -45,7 +45,8 @@
 //    of tiles of the same (batch, head) and the K/V of that head stay in the
 //    XCD's L2 (the pages' L2 swizzle, talk notes "Implementation details",
 //    made XCD-aware); causal and PrefixLM grids start with the heaviest query
-//    tiles.
+//    tiles, and under the document mask an optional order computed from the
+//    document ids (doc_order.hip) does the same.
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
@@ -103,7 +104,19 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     mt_lin = ti.mt_lin;
     bh = ti.bh;
   } else {
-    const int L = xcd_remap(blockIdx.x, a.total);
+    int L = -1;
+    if constexpr (MK == MK_DOC) {
+      if (a.doc_order != nullptr) {
+        // heaviest-first order of the (b, query tile) pairs; the query heads
+        // of one pair are consecutive blocks, so with Hq a multiple of 8 every
+        // XCD keeps the same heads (and their keys in its L2) throughout
+        static_assert(BM == kDocTileM && BN == kDocTileN, "document order tile sizes");
+        const int item = a.doc_order[blockIdx.x / a.Hq];
+        if (item < 0 || item >= a.B * a.nM) return;  // not an order of this shape: touch nothing
+        L = ((item / a.nM) * a.Hq + blockIdx.x % a.Hq) * a.nM + item % a.nM;
+      }
+    }
+    if (L < 0) L = xcd_remap(blockIdx.x, a.total);
     mt_lin = L % a.nM;
     bh = L / a.nM;
   }

@@ -70,6 +70,22 @@ const char* av_status_string(int status) {
   return "unknown av_status";
 }
 
+int attn_doc_order_len(int B, int S) {
+  if (B <= 0 || S < 0) return AV_ERR_SHAPE;
+  const int64_t n = (int64_t)B * (((int64_t)S + av::kDocTileM - 1) / av::kDocTileM);
+  return n > av::kDocOrderMax ? AV_ERR_TOO_LARGE : (int)n;
+}
+
+int attn_doc_order(const int32_t* doc_id, int B, int S, int32_t* order, int order_len, hipStream_t stream) {
+  const int n = attn_doc_order_len(B, S);
+  if (n < 0) return n;
+  if (n == 0) return AV_OK;
+  if (doc_id == nullptr || order == nullptr) return AV_ERR_NULL;
+  if (!aligned(doc_id, 4) || !aligned(order, 4)) return AV_ERR_ALIGN;
+  if (order_len < n) return AV_ERR_WORKSPACE;
+  return hip_status(av::launch_doc_order(doc_id, B, S, order, stream));
+}
+
 int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse, int B,
              int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
   if (var == nullptr) return AV_ERR_NULL;
@@ -95,6 +111,8 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
   if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
+  if (var->doc_order != nullptr && var->mask != AV_MASK_DOCUMENT) return AV_ERR_PARAM;
+  if (var->doc_order != nullptr && !aligned(var->doc_order, 4)) return AV_ERR_ALIGN;
   // bias rows are read 8 bytes at a time when Skv % 4 == 0: every slice must
   // then start on an 8-byte boundary
   if (tbias && (!aligned(var->bias, 8) ||
@@ -119,6 +137,7 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.o = out;
   a.lse = lse;
   a.doc = var->doc_id;
+  a.doc_order = var->mask == AV_MASK_DOCUMENT ? var->doc_order : nullptr;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

@@ -28,6 +28,7 @@ struct AttnArgs {
   void* o;
   float* lse;        // nullable
   const int* doc;    // MK_DOC only
+  const int* doc_order;  // MK_DOC, nullable: (b * nM + query tile) in visiting order
   const void* bias;  // SM_BIAS / SM_TBIAS: bf16, rows of Skv; (b, hq) slice at b * bias_bs + hq * bias_hs
   const void* gate;  // SM_BIAS: [B, Hq, Sq, D] bf16 gate pre-activations (same layout as q)
   int B, Hq, Hkv, Sq, Skv;
@@ -62,6 +63,17 @@ constexpr int attn_qb(int D, int sm, int mask) {
 }
 constexpr int attn_bm(int D, int sm, int mask) { return 4 * 32 * attn_qb(D, sm, mask); }
 constexpr int kAttnBMMax = 256;
+
+// Work order of the document mask: query tiles of kDocTileM rows (the
+// fused kernel's tile under that mask at every D and score modifier), key
+// tiles of kDocTileN, at most kDocOrderMax query tiles per order.
+constexpr int kDocTileM = attn_bm(64, SM_NONE, MK_DOC);
+constexpr int kDocTileN = 64;
+constexpr int kDocOrderMax = 16384;
+static_assert(attn_bm(32, SM_NONE, MK_DOC) == kDocTileM && attn_bm(128, SM_NONE, MK_DOC) == kDocTileM &&
+                  attn_bm(64, SM_TBIAS, MK_DOC) == kDocTileM,
+              "one query tile height under the document mask");
+hipError_t launch_doc_order(const int* doc, int B, int S, int* order, hipStream_t stream);
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
 // Evoformer gated attention over the projected workspace (D = 32): row-wise

@@ -268,18 +268,28 @@ def run_sweep(path, steps, warmup):
             doc = torch.from_numpy(doc_np).to(dev)
             doc_lens = wi.doc_lengths(4, B, S)
             cases = [("none", "none"), ("alibi", "none"), ("softcap", "none")] if Hkv == 16 else []
-            cases += [("none", "causal"), ("none", "sliding_window"), ("none", "prefix_lm"), ("none", "document")]
-            for sm, mk in cases:
+            cases += [("none", "causal"), ("none", "sliding_window"), ("none", "prefix_lm"), ("none", "document"),
+                      ("none", "document+order")]
+            # the document mask's heaviest-first work order: built once per
+            # document layout (its own time is reported), reused by every call
+            order = av.attn_doc_order(doc)
+            _, per_order = time_launches([lambda: av.attn_doc_order(doc, out=order)], steps, warmup)
+            for sm, case in cases:
+                mk = case.split("+")[0]
                 kw = dict(score_mod=sm, mask=mk, window=256, prefix_len=S // 4,
-                          doc_id=doc if mk == "document" else None, out=out)
+                          doc_id=doc if mk == "document" else None, out=out,
+                          doc_order=order if case == "document+order" else None)
                 _, per = time_launches([lambda kw=kw: av.attn_fwd(q, k, v, **kw)], steps, warmup)
                 fl = attn_flops(B, 16, S, 64, mk, window=256, prefix_len=S // 4, doc_lens=doc_lens)
                 by = attn_bytes(B, 16, Hkv, S, 64)
                 tf = fl / (per[0] * 1e-3) / 1e12
-                emit({"kernel": "attn_fwd", "score_mod": sm, "mask": mk, "B": B, "Hq": 16, "Hkv": Hkv, "S": S,
-                      "D": 64, "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
-                      "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                      "hbm_gbs": round(by / (per[0] * 1e-3) / 1e9, 1)})
+                rec = {"kernel": "attn_fwd", "score_mod": sm, "mask": case, "B": B, "Hq": 16, "Hkv": Hkv, "S": S,
+                       "D": 64, "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
+                       "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "hbm_gbs": round(by / (per[0] * 1e-3) / 1e9, 1)}
+                if case == "document+order":
+                    rec["order_build_us"] = round(per_order[0] * 1e3, 2)
+                emit(rec)
     # the bias-tensor score modifier at S = 4096: one bias per head shared over
     # the batch ([1, 16, S, S], 537 MB) and one per (batch, head) ([4, 16, S, S], 2.1 GB)
     S, B = 4096, 4

@@ -98,6 +98,12 @@ typedef struct {
   const void* bias;
   int64_t bias_batch_stride;
   int64_t bias_head_stride;
+  /* AV_MASK_DOCUMENT, optional (NULL = natural order): device int32 order of
+   * the query tiles written by attn_doc_order for the same doc_id, B and S,
+   * holding attn_doc_order_len(B, S) entries.  It changes only the order in
+   * which attn_fwd visits its work, never a result bit.  Non-NULL with any
+   * other mask is AV_ERR_PARAM; 4-byte aligned.  Read by attn_fwd only. */
+  const int32_t* doc_order;
 } av_variant;
 
 /* Fused attention forward, MHA and GQA.
@@ -115,6 +121,30 @@ typedef struct {
  * and out, must be smaller than 2 GiB. */
 int attn_fwd(const av_variant* variant, const void* q, const void* k, const void* v, void* out,
              float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream);
+
+/* Work order of attn_fwd under the document mask (one of the masked variants
+ * of talk notes, "Evaluation: FlexAttention-supported variants"; like
+ * FlexAttention's block_mask in "Comparison with FlexAttention", it is built
+ * once from the mask's data and reused across calls, but it skips nothing:
+ * the key ranges stay analytic).  A query
+ * tile there attends to the keys of its own documents, so its run time
+ * follows the document lengths; visiting the heaviest tiles first shortens
+ * the tail that heavy tiles starting late would leave.  attn_doc_order
+ * writes the n = attn_doc_order_len(B, S) query tiles (b * ceil(S/128) + t
+ * for 128-row tile t of sequence b) sorted by the number of 64-key tiles
+ * their documents span, largest first, ties by ascending index.  The order
+ * depends only on doc_id: compute it once per document layout and pass it
+ * as av_variant.doc_order to every attn_fwd call (layer, head count, score
+ * modifier, D) over that layout.
+ *   doc_id [B, S] int32 device, non-decreasing rows (as av_variant.doc_id)
+ *   order  [order_len] int32 device, caller-owned, 4-byte aligned; the
+ *          first n entries are written
+ * attn_doc_order_len returns n, or AV_ERR_SHAPE (B <= 0, S < 0) or
+ * AV_ERR_TOO_LARGE (n > 16384, i.e. more than 2^21 tokens).  attn_doc_order
+ * returns those errors, AV_ERR_NULL, AV_ERR_ALIGN, AV_ERR_WORKSPACE when
+ * order_len < n; n == 0 launches nothing. */
+int attn_doc_order_len(int B, int S);
+int attn_doc_order(const int32_t* doc_id, int B, int S, int32_t* order, int order_len, hipStream_t stream);
 
 /* Decoding / short-query attention forward (split over the keys).  The
  * pages' serving workload decodes causal and softcapped LLaMA-3.2-1B variants
@@ -241,7 +271,7 @@ int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, 
 const char* av_status_string(int status);
 
 /* ABI version of this header; bumped when a signature or struct changes. */
-#define AV_ABI_VERSION 2
+#define AV_ABI_VERSION 3
 int av_abi_version(void);
 
 #ifdef __cplusplus

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.av_abi_version() == 2
+    assert lib.av_abi_version() == 3
     for code, name in av.STATUS.items():
         assert lib.av_status_string(code).decode().startswith(name)
     assert lib.av_status_string(12345).decode() == "unknown av_status"
@@ -122,6 +122,36 @@ def test_bias_score_mod_rejections(lib):
     assert lib.attn_decode_fwd(ref, P, P2, P3, P4, None, 0x200000, 1 << 30, 1, 32, 8, 1, 4096, 64, None) == -3
     assert lib.attn_bwd(ref, P, P2, P3, P4, 0x70000, P, P2, P3, 0x200000, 1 << 30, 1, 2, 2, 64, 64, 64,
                         None) == -3
+
+
+def test_doc_order_rejections(lib):
+    assert lib.attn_doc_order_len(0, 128) == -2
+    assert lib.attn_doc_order_len(2, -1) == -2
+    assert lib.attn_doc_order_len(1, 0) == 0
+    assert lib.attn_doc_order_len(4, 4096) == 4 * 32
+    assert lib.attn_doc_order_len(3, 129) == 3 * 2                  # ragged last tile
+    assert lib.attn_doc_order_len(1, 16384 * 128) == 16384          # the largest order
+    assert lib.attn_doc_order_len(1, 16384 * 128 + 1) == -8
+    assert lib.attn_doc_order_len(2, 2**31 - 1) == -8               # no int overflow
+    assert lib.attn_doc_order(None, 1, 0, None, 0, None) == 0       # empty: nothing launched
+    assert lib.attn_doc_order(None, 2, 256, P2, 4, None) == -1
+    assert lib.attn_doc_order(P, 2, 256, None, 4, None) == -1
+    assert lib.attn_doc_order(P + 2, 2, 256, P2, 4, None) == -4
+    assert lib.attn_doc_order(P, 2, 256, P2 + 2, 4, None) == -4
+    assert lib.attn_doc_order(P, 2, 256, P2, 3, None) == -5          # order_len < B * ceil(S/128)
+    assert lib.attn_doc_order(P, 0, 256, P2, 4, None) == -2
+    assert lib.attn_doc_order(P, 200, 16384, P2, 1 << 30, None) == -8
+    # attn_fwd takes an order only with the document mask, 4-byte aligned
+    v = av.make_variant(mask="causal")
+    v.doc_order = 0x80000
+    assert _attn(lib, v) == -7
+    v = av.make_variant(mask="document")
+    v.doc_id = 0x90000
+    v.doc_order = 0x80002
+    assert _attn(lib, v) == -4
+    assert av.attn_doc_order_len(4, 4096) == 128
+    with pytest.raises(RuntimeError):
+        av.attn_doc_order_len(1, 16384 * 128 + 1)
 
 
 def test_diff_attn_rejections(lib):
