@@ -494,6 +494,22 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "bias", "B": B, "H": H, "S": S, "bias": [1, H, S, S], "launches": steps}))
         return
+    if what == "document":
+        # document mask at S = 4096 (16 heads, seeded lengths 64..S/2): the
+        # heaviest-first order is built once per step, then the ordered forward
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        doc = torch.from_numpy(wi.doc_ids(4, B, S)).to(dev)
+        order = av.attn_doc_order(doc)
+        out = torch.empty_like(q)
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.attn_doc_order(doc, out=order)
+            av.attn_fwd(q, k, v, mask="document", doc_id=doc, doc_order=order, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "document", "B": B, "H": H, "S": S, "D": D, "launches": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -526,6 +542,7 @@ def main():
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
+                                          "document",
                                           "decode", "decode_b1", "bwd", "bias"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
