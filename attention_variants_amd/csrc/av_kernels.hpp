@@ -44,8 +44,8 @@ struct AttnArgs {
   int fixed_ref;     // softcap with 2 * cap * log2(e) <= 96: exponent reference fixed at the cap
   long long bias_bs, bias_hs;  // bias element strides of batch and head (0 = shared)
   // fixed-reference softcap: t - cap*log2(e) = fma(raw, P(raw^2), -cap*log2(e)) with the
-  // quadratic P below, valid while |raw| <= sc_poly_lim (raw = unscaled q.k)
-  float sc_poly[3];
+  // linear P below, valid while |raw| <= sc_poly_lim (raw = unscaled q.k)
+  float sc_poly[2];
   float sc_poly_lim;
 };
 

@@ -251,7 +251,7 @@ def test_score_mod_S16384_rms(gpu_lib, score_mod):
 @pytest.mark.parametrize("D,mask", [(64, "none"), (64, "causal"), (32, "document"), (128, "prefix_lm")])
 def test_softcap_score_ranges(gpu_lib, qmul, D, mask):
     """Softcap (cap 20, fixed reference) with Q scaled by a power of two: small
-    scores (every tile on the polynomial form), scores that reach past 0.5 cap
+    scores (every tile on the polynomial form), scores that reach past 0.25 cap
     in some tiles (mixed forms), and scores far into saturation (exact form)."""
     B, H, S = 2, 4, 300
     x = wi.attention_inputs(B, H, H, S, S, D, seeds=(31, 32, 33))
