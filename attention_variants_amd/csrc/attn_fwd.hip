@@ -93,6 +93,18 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   bf16 (*Vs)[BN * D] = reinterpret_cast<bf16 (*)[BN * D]>(lds_raw + 2 * BN * KP * 2);  // swizzled for transposed reads
   bf16* QOs = reinterpret_cast<bf16*>(lds_raw);
   __shared__ __attribute__((aligned(16))) int Ds[2][MK == MK_DOC ? BN : 1];
+  // Bias tile (BM query rows x BN keys) staged through LDS at D <= 64: loaded
+  // with the K/V tile as coalesced 16-byte row chunks, double-buffered, row
+  // pitch BN + 4 elements (136 bytes: the 32 rows one 8-byte transposed-order
+  // read touches fall in 32 distinct bank pairs).  At D = 128 the two
+  // buffers would halve the resident workgroups; there each lane loads its
+  // own bias from memory one tile ahead.
+  constexpr bool kBiasLds = kBias && D <= 64;
+  constexpr int BP = BN + 4;
+  constexpr int BCH = BM * (BN / 8) / NT;  // 16-byte bias chunks per thread per tile
+  static_assert(!kBiasLds || (QB == 1 && BCH >= 1 && BM * (BN / 8) % NT == 0), "bias tile/thread mismatch");
+  static_assert(SM != SM_BIAS || kBiasLds, "the pair bias enters the MFMA from the staged tile");
+  __shared__ __attribute__((aligned(16))) bf16 Bs[kBiasLds ? 2 : 1][kBiasLds ? BM * BP : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -116,9 +128,23 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         L = ((item / a.nM) * a.Hq + blockIdx.x % a.Hq) * a.nM + item % a.nM;
       }
     }
-    if (L < 0) L = xcd_remap(blockIdx.x, a.total);
-    mt_lin = L % a.nM;
-    bh = L / a.nM;
+    if (L >= 0) {
+      mt_lin = L % a.nM;
+      bh = L / a.nM;
+    } else {
+      L = xcd_remap(blockIdx.x, a.total);
+      if (SM == SM_TBIAS && a.bias_bs == 0) {
+        // bias shared over the batch: the batch entries of one (head, query
+        // tile) are consecutive blocks, so they run together on one XCD and
+        // read each bias row from its L2 instead of once per batch entry
+        const int r = L / a.B;
+        mt_lin = r % a.nM;
+        bh = (L % a.B) * a.Hq + r / a.nM;
+      } else {
+        mt_lin = L % a.nM;
+        bh = L / a.nM;
+      }
+    }
   }
   // Evoformer (pair bias shared over the batch): heads outermost, so one XCD's
   // run of tiles covers few heads and their bias stays in its L2.
@@ -263,6 +289,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   };
 
   i32x4 kr[NCH], vr[NCH];
+  i32x4 br[kBiasLds ? BCH : 1];
   int dr = 0;
   auto gload = [&](int nt) {
 #pragma unroll
@@ -272,6 +299,26 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       const uint32_t off = (uint32_t)((nt * BN + row) * D + col * 8) * 2;
       kr[c] = buf_load16(krs, off);
       vr[c] = buf_load16(vrs, off);
+    }
+    if constexpr (kBiasLds) {
+      // rows q0 + row, keys nt*BN + 8*col ..; rows past Sq read as zero (buffer
+      // bounds), keys past Skv belong to partial tiles, whose mask drops them
+#pragma unroll
+      for (int c = 0; c < BCH; ++c) {
+        const int idx = tid + NT * c;
+        const int row = idx / (BN / 8), col = idx % (BN / 8);
+        const uint32_t off = (uint32_t)((q0 + row) * a.Skv + nt * BN + col * 8) * 2;
+        if (a.Skv % 8 == 0) {
+          br[c] = buf_load16(brs, off);
+        } else {  // rows not 16-byte aligned: 16-bit loads
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, off + 4 * e, 0, 0);
+            const uint32_t x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(brs, off + 4 * e + 2, 0, 0);
+            br[c][e] = (int)(x0 | (x1 << 16));
+          }
+        }
+      }
     }
     if constexpr (MK == MK_DOC) {
       if (tid < BN) {
@@ -288,6 +335,16 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       *(i32x4*)&Ks[buf][row * KP + col * 8] = kr[c];
       *(i32x4*)&Vs[buf][tr_tile_off<D>(row, col * 8)] = vr[c];
     }
+    if constexpr (kBiasLds) {
+#pragma unroll
+      for (int c = 0; c < BCH; ++c) {
+        const int idx = tid + NT * c;
+        const int row = idx / (BN / 8), col = idx % (BN / 8);
+        bf16* dst = &Bs[buf][row * BP + col * 8];  // 8-byte aligned (the pitch is 136 bytes)
+        *(i32x2*)dst = i32x2{br[c][0], br[c][1]};
+        *(i32x2*)(dst + 4) = i32x2{br[c][2], br[c][3]};
+      }
+    }
     if constexpr (MK == MK_DOC) {
       if (tid < BN) Ds[buf][tid] = dr;
     }
@@ -295,7 +352,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
   // bias of this lane's (query, key) elements: keys n0 + 4*hh + 32*kb +
   // 8*g + 0..3, loaded one tile ahead of its use
-  i32x4 braw[QB][NKB * 2];
+  i32x4 braw[QB][kBiasLds ? 1 : NKB * 2];
   auto bias_load = [&](int n0) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -325,12 +382,24 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   // scores are q.k*scale + bias (natural units); the other modifiers produce log2 units
   const float cexp = kBias ? kLog2e : a.c;
 
-  // S^T = K Q^T of LDS tile buf for every query block
-  auto qk = [&](f32x16 (&s)[QB][NKB], int buf) {
+  // S^T = K Q^T of LDS tile buf for every query block; with the Evoformer
+  // pair bias (q already scaled) the accumulators start at the bias instead
+  // of zero, so the MFMA adds it
+  auto qk = [&](f32x16 (&s)[QB][NKB], int buf, const i32x2* bq) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][kb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) {
+        if constexpr (SM == SM_BIAS) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {  // bf16 -> fp32 is a 16-bit shift
+            const int wd = bq[kb * 4 + (j >> 2)][(j & 3) >> 1];
+            s[qb][kb][j] = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
+          }
+        } else {
+          s[qb][kb] = f32x16{};
+        }
+      }
       const bf16* krow = Ks[buf] + (kb * 32 + l32) * KP + hh * 8;
 #pragma unroll
       for (int st_ = 0; st_ < NDS; ++st_) {
@@ -349,8 +418,15 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
     // ---- S^T = K Q^T : s[qb][kb] holds keys kb*32 + 8*(j/4) + 4*hh + j%4 of query qi[qb];
     //      each K fragment read from LDS feeds the MFMAs of every query block
+    // staged bias of this lane's elements: row qi - q0, keys 32*kb + 8*g + 4*hh + 0..3
+    i32x2 bq[kBiasLds ? NKB * 4 : 1];
+    if constexpr (kBiasLds) {
+      const bf16* brow = Bs[buf] + (qi[0] - q0) * BP + 4 * hh;
+#pragma unroll
+      for (int g = 0; g < NKB * 4; ++g) bq[g] = *(const i32x2*)(brow + 8 * g);
+    }
     f32x16 s[QB][NKB];
-    qk(s, buf);
+    qk(s, buf, bq);
 
     // ---- fixed-reference softcap: the polynomial form in place; a tile with
     //      a raw score outside its range (wave-uniform, rare) recomputes
@@ -366,7 +442,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 #pragma unroll
           for (int j = 0; j < 16; ++j) s[qb][kb][j] = softcap_poly(s[qb][kb][j]);
       if (any_lane(amax > a.sc_poly_lim)) {
-        qk(s, buf);
+        qk(s, buf, bq);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -380,7 +456,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     for (int qb = 0; qb < QB; ++qb) {
       // ---- score modifier: ALiBi and softcap in log2 units, bias in natural
       //      units (q.k*scale + bias); vanilla keeps the raw q.k, its scale folded into exp2
-      if constexpr (SM != SM_NONE && SM != SM_GATE && SM != SM_SOFTCAP_FIXED) {
+      if constexpr (SM != SM_NONE && SM != SM_GATE && SM != SM_SOFTCAP_FIXED && SM != SM_BIAS) {
         // ALiBi goes straight to the exponent argument, relative to the
         // current reference: s*c + slope*(key - query) - m_sub
         float ab[4];
@@ -397,7 +473,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
             } else if constexpr (SM == SM_SOFTCAP) {
               s[qb][kb][j] = softcap_t(s[qb][kb][j]);
             } else {  // bias: bf16 -> fp32 is a 16-bit shift
-              const int wd = braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
+              const int wd = kBiasLds ? bq[kb * 4 + (j >> 2)][(j & 3) >> 1]
+                                      : braw[qb][(kb * 4 + (j >> 2)) >> 1][((j >> 2) & 1) * 2 + ((j & 3) >> 1)];
               const float bv = __builtin_bit_cast(float, (j & 1) ? (wd & (int)0xffff0000) : (wd << 16));
               s[qb][kb][j] = fmaf(s[qb][kb][j], a.scale, bv);
             }
@@ -531,7 +608,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   auto tile_at = [&](int it) { return kDescending ? n_hi - 1 - (it - n_lo) : it; };
 
   if (n_lo < n_hi) gload(tile_at(n_lo));
-  if constexpr (kBias) {
+  if constexpr (kBias && !kBiasLds) {
     if (n_lo < n_hi) bias_load(tile_at(n_lo) * BN);
   }
 
@@ -563,7 +640,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     if (!__builtin_amdgcn_readfirstlane((int)skip)) tile(__builtin_amdgcn_readfirstlane((int)full) != 0, buf, n0);
     // the bias is loaded one tile ahead, also after a tile this wave skips,
     // so that every processed tile finds its own bias in braw
-    if constexpr (kBias) {
+    if constexpr (kBias && !kBiasLds) {
       if (it + 1 < n_hi) bias_load(tile_at(it + 1) * BN);
     }
   }

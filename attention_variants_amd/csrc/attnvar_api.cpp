@@ -451,8 +451,7 @@ int evoformer_launch(const void* m, const void* wq, const void* wk, const void* 
   a.H = H;
   a.dh = dh;
   a.col = col;
-  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)dh);
-  a.c = (float)(sc * kLog2e);
+  a.scale = scale > 0.f ? scale : (float)(1.0 / sqrt((double)dh));
   return hip_status(av::launch_evoformer(a, stream));
 }
 

@@ -7,8 +7,9 @@
 
 namespace av {
 
-// Internal score modifiers: SM_BIAS = Evoformer pair bias added to the scaled
-// score, with the sigmoid-gate epilogue and a token-major [B, Sq, Hq*D]
+// Internal score modifiers: SM_BIAS = Evoformer pair bias added to the score
+// of queries that arrive already scaled (the projection folds the softmax
+// scale into q), with the sigmoid-gate epilogue and a token-major [B, Sq, Hq*D]
 // output (row-wise form); SM_GATE = no modifier, sigmoid-gate epilogue and a
 // token-major [Sq, B, Hq*D] output (column-wise form: problem b is residue
 // column b, query q is sequence q); SM_SOFTCAP_FIXED = softcap whose exponent
@@ -166,7 +167,7 @@ struct EvoArgs {
   void* ws;          // 4 planes (q, k, v, g) bf16: [Ns, H, Nr, dh] row-wise, [Nr, H, Ns, dh] column-wise
   int Ns, Nr, Cm, H, dh;
   int col;           // 0: row-wise (pair bias), 1: column-wise (no bias)
-  float c;           // scale * log2(e)
+  float scale;       // softmax scale, applied to q in the projection epilogue
 };
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh);
 hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream);

@@ -14,7 +14,10 @@
 //     channels, K = Cm.  It computes C^T = W^T m^T so that each lane ends up
 //     holding 4 consecutive channels of one token; results are rounded to
 //     bf16 and scattered head-major into the workspace as four planes
-//     [Ns, H, Nr, dh] (q, k, v, g).
+//     [Ns, H, Nr, dh] (scale*q, k, v, g).  The softmax scale is applied to q
+//     in fp32 before its one bf16 rounding, so the attention kernel's raw
+//     scores are already scaled and the pair bias becomes the initial
+//     accumulator of the QK^T MFMA.
 //  2. the fused attention kernel at D = dh = 32 with the pair bias as score
 //     modifier and the sigmoid gate + token-major store as epilogue; each
 //     (sequence, head, 128-residue tile) is one workgroup, sequences vary
@@ -173,6 +176,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const E
   // contiguous run.
   __syncthreads();  // every wave is done with the staging tiles
   bf16* Cs = lds;
+  const float os = p == 0 ? a.scale : 1.f;  // q plane: softmax scale folded in
 #pragma unroll
   for (int mb2 = 0; mb2 < MB; ++mb2) {
     const int tl = wm * MB * 32 + mb2 * 32 + l32;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const E
       for (int g4 = 0; g4 < 4; ++g4) {
         bf16x4 val;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) val[q] = (bf16)acc[nb][mb2][g4 * 4 + q];
+        for (int q = 0; q < 4; ++q) val[q] = (bf16)(acc[nb][mb2][g4 * 4 + q] * os);
         *(bf16x4*)&Cs[tl * CP + wn * 64 + nb * 32 + 8 * g4 + 4 * hh] = val;
       }
     }
@@ -251,8 +255,8 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   const int bm = attn_bm(32, a.col ? SM_GATE : SM_BIAS, MK_NONE);
   t.nM = (L + bm - 1) / bm;
   t.total = nB * a.H * t.nM;
-  t.c = a.c;
-  t.scale = a.c / 1.4426950408889634f;
+  t.c = kLog2e;  // q arrives scaled
+  t.scale = 1.f;
   t.softcap = 1.f;
   return launch_evo_attention(t, a.col, stream);
 }

@@ -245,7 +245,8 @@ int diff_head_fwd(const void* q, const void* k, const void* v, const float* lamb
  *   out  [Ns, Nr, H*dh]
  * The projections are computed into `workspace` (bf16, owned by the caller,
  * at least evoformer_workspace_bytes(...) bytes, 256-byte aligned) by one
- * kernel, then consumed by the attention kernel.  scale = 0 selects
+ * kernel, then consumed by the attention kernel; the q plane holds scale*q
+ * (the softmax scale applied before the bf16 rounding).  scale = 0 selects
  * 1/sqrt(dh).  Supported: dh = 32, Cm a multiple of 64, H*dh a multiple of 128. */
 size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh);
 int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
