@@ -290,6 +290,11 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
 
   i32x4 kr[NCH], vr[NCH];
   i32x4 br[kBiasLds ? BCH : 1];
+  // 16-byte bias loads need 16-byte aligned rows: Skv a multiple of 8 and an
+  // aligned slice base (the ABI guarantees 8 bytes)
+  const bool bias_rows16 = kBiasLds && a.Skv % 8 == 0 &&
+                           (reinterpret_cast<uintptr_t>((const bf16*)a.bias + (size_t)b * a.bias_bs +
+                                                        (size_t)hq * a.bias_hs) & 15) == 0;
   int dr = 0;
   auto gload = [&](int nt) {
 #pragma unroll
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         const int idx = tid + NT * c;
         const int row = idx / (BN / 8), col = idx % (BN / 8);
         const uint32_t off = (uint32_t)((q0 + row) * a.Skv + nt * BN + col * 8) * 2;
-        if (a.Skv % 8 == 0) {
+        if (bias_rows16) {
           br[c] = buf_load16(brs, off);
         } else {  // rows not 16-byte aligned: 16-bit loads
 #pragma unroll

@@ -127,3 +127,23 @@ def test_benchmark_shape_sampled(gpu_lib, mask):
 
 def test_full_bias_larger(gpu_lib):
     _run(gpu_lib, 2, 4, 4, 1024, 64, "causal", "full", rows=sample_rows(1024, tiles=(128,), extra=16, seed=9))
+
+
+def test_bias_base_8_byte_aligned(gpu_lib):
+    """A bias whose storage starts 8 bytes past a 16-byte boundary (the ABI
+    asks for 8-byte alignment), with Skv a multiple of 8: every (b, h) slice
+    then starts at 8 mod 16, where the staged bias tile must read its rows
+    with narrower loads than its 16-byte row chunks."""
+    B, H, S, D = 2, 4, 136, 64
+    x = wi.attention_inputs(B, H, H, S, S, D)
+    bb = wi.normal_bf16(18, (B, H, S, S), 2.0)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    store = torch.zeros(bb.size + 4, dtype=torch.bfloat16, device="cuda")
+    bias = store[4:].view(B, H, S, S)
+    bias.copy_(to_dev(bb))
+    assert bias.data_ptr() % 16 == 8
+    for mask in ("none", "causal"):
+        out = gpu_lib.attn_fwd(q, k, v, score_mod="bias", mask=mask, bias=bias)
+        torch.cuda.synchronize()
+        ref, _ = oracle.attention(f64(x["q"]), f64(x["k"]), f64(x["v"]), score_mod="bias", mask=mask, bias=f64(bb))
+        assert_close(out.float().cpu().numpy(), ref, f"bias at 8 mod 16 bytes, {mask}")
