@@ -40,6 +40,8 @@ KERNEL_SOURCES = (
     "attention_variants_amd/csrc/attn_fwd.hip",
     "attention_variants_amd/csrc/attn_tile.hpp",
     "attention_variants_amd/csrc/av_device.hpp",
+    "attention_variants_amd/csrc/av_kernels.hpp",    # the kernel's argument block and tile shapes
+    "attention_variants_amd/csrc/attnvar_api.cpp",   # launch choices and host-computed constants (softcap form)
 )
 
 
