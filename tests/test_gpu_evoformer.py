@@ -76,3 +76,22 @@ def test_benchmark_shapes(gpu_lib, Nr):
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([[0, 1, Nr - 1, 127, 128, Nr // 2], rng.integers(0, Nr, 40)]))
     _run(gpu_lib, 128, Nr, seqs=seqs, rows=rows)
+
+
+def test_pair_bias_minus_inf(gpu_lib):
+    """A pair bias of -inf drops the pair (the bias enters the QK^T MFMA as its
+    initial accumulator, where -inf stays -inf); about a third of the pairs
+    are dropped, each row keeps its own residue."""
+    Ns, Nr, Cm, H, dh = 3, 100, 128, 4, 32
+    x = wi.evoformer_inputs(Ns, Nr, Cm, H, dh)
+    drop = np.random.default_rng(41).random((H, Nr, Nr)) < 0.35
+    drop[:, np.arange(Nr), np.arange(Nr)] = False
+    x["bias"] = np.where(drop, np.uint16(0xFF80), x["bias"]).astype(np.uint16)
+    t = {n: to_dev(x[n]) for n in x}
+    out = gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=H, dh=dh)
+    torch.cuda.synchronize()
+    ref = oracle.evoformer_row_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]), f64(x["wg"]),
+                                               f64(x["bias"]), H=H, dh=dh)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "evoformer pair bias with -inf")
