@@ -95,8 +95,8 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) int Ds[2][MK == MK_DOC ? BN : 1];
   // Bias tile (BM query rows x BN keys) staged through LDS at D <= 64: loaded
   // with the K/V tile as coalesced 16-byte row chunks, double-buffered, row
-  // pitch BN + 4 elements (136 bytes: the 32 rows one 8-byte transposed-order
-  // read touches fall in 32 distinct bank pairs).  At D = 128 the two
+  // pitch BN + 4 elements (136 bytes: the 32 query rows that one 8-byte-per-
+  // lane read touches fall in 32 distinct bank pairs).  At D = 128 the two
   // buffers would halve the resident workgroups; there each lane loads its
   // own bias from memory one tile ahead.
   constexpr bool kBiasLds = kBias && D <= 64;
