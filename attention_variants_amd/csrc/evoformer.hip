@@ -213,6 +213,154 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const E
   }
 }
 
+// Persistent form for Cm = 256: one workgroup per CU keeps a 256 x 128 W
+// tile (one projection's 128 channels) resident and streams 128-token tiles
+// of m past it, the next tile's loads in flight in registers during the
+// current tile's MFMAs.  W passes through LDS once; each wave then holds the
+// W^T operands of its 64 channels for the whole K in registers (128 VGPRs),
+// so the per-tile LDS traffic is the m tile and the C tile only.  A workgroup's life is then many token tiles instead
+// of four 64-wide K chunks.  Block b runs on XCD b % 8; the 32 blocks of an
+// XCD are the Nt channel tiles of 32 / Nt token streams, so the channel tiles
+// of one token tile run side by side on one XCD and read its m rows from
+// that XCD's L2.
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also waits
+// for the workgroup's outstanding global stores, which would hold every token
+// tile of the persistent loop behind the previous tile's output writes.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+constexpr int PP_K = 256;            // Cm of this form
+constexpr int PP_MP = PP_K + 8;      // m tile pitch: 16 consecutive rows -> 16 distinct 16-byte bank groups
+constexpr int PP_BLOCKS = 256;       // 8 XCDs x 32 CUs
+__global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoArgs a) {
+  constexpr int NT = 512, GM = 128, GN = 128, WN = GN / 64, MB = 1;
+  constexpr int MCH = GM * PP_K / 8 / NT;  // 16-byte m chunks per thread per token tile
+  constexpr int WCH = PP_K * GN / 8 / NT;  // 16-byte W chunks per thread
+  constexpr int CP = GN + 8;               // C tile pitch
+  static_assert(MCH * NT * 8 == GM * PP_K && WCH * NT * 8 == PP_K * GN, "tile/thread mismatch");
+  static_assert(GM * CP <= GM * PP_MP, "the C tile reuses the m tile's bytes");
+  __shared__ __attribute__((aligned(16))) bf16 Ws[PP_K * GN];
+  __shared__ __attribute__((aligned(16))) bf16 Ms[GM * PP_MP];
+  bf16* const Cs = Ms;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int HD = a.H * a.dh, N = 4 * HD, M = a.Ns * a.Nr;
+  const int Nt = N / GN;                   // channel tiles; the launcher checks that Nt divides 32
+  const int Mt = (M + GM - 1) / GM;
+  const int spx = 32 / Nt;                 // token streams per XCD
+  const int x = blockIdx.x % 8, r = blockIdx.x / 8;
+  const int nt = r % Nt;
+  const int streams = 8 * spx;
+  const int stream = x * spx + r / Nt;
+  const int n0 = nt * GN, p = n0 / HD, c0 = n0 % HD;
+  const int wn = w % WN, wm = w / WN;
+  const int Linner = a.col ? a.Ns : a.Nr;  // token order as in evo_proj_kernel
+  const uint32_t m_bytes = (uint32_t)M * a.Cm * 2;
+  const auto mrs = make_rsrc(a.m, m_bytes);
+  const auto wrs = make_rsrc(a.w[p], (uint32_t)a.Cm * HD * 2);
+
+  // resident W tile (stored before the first barrier of the loop)
+#pragma unroll
+  for (int c = 0; c < WCH; ++c) {
+    const int idx = tid + NT * c;
+    const int wrow = idx / (GN / 8), wcol = idx % (GN / 8);
+    const i32x4 v = buf_load16(wrs, (uint32_t)(wrow * HD + c0 + wcol * 8) * 2);
+    *(i32x4*)&Ws[w_off<GN>(wrow, wcol * 8)] = v;
+  }
+
+  i32x4 mr[MCH];
+  auto mload = [&](int mt) {
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int idx = tid + NT * c;
+      const int tl = idx / (PP_K / 8), kc = idx % (PP_K / 8);
+      const int t = mt * GM + tl;
+      const int row = a.col ? (t % a.Ns) * a.Nr + t / a.Ns : t;
+      const uint32_t off = t < M ? (uint32_t)row * a.Cm * 2 + kc * 16 : m_bytes;  // past M: zeros
+      mr[c] = buf_load16(mrs, off);
+    }
+  };
+
+  const int wr_row = 8 * hh + ((lane & 15) >> 2);
+  const int wr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int wr_xo = w_swz((lane & 15) >> 2) << 5;
+  const float os = p == 0 ? a.scale : 1.f;  // q plane: softmax scale folded in
+  const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
+  const auto ors = make_rsrc((bf16*)a.ws + (size_t)p * plane, (uint32_t)(plane * 2));
+  const int h0 = c0 / 32;
+
+  if (stream < Mt) mload(stream);
+  lds_barrier();  // W is stored
+  bf16x8 wa[PP_K / 16][2];
+#pragma unroll
+  for (int ks = 0; ks < PP_K / 16; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const bf16* wp = &Ws[(ks * 16 + wr_row) * GN + ((wn * 64 + nb * 32 + wr_col) ^ wr_xo)];
+      const i16x4 lo = lds_read_tr16(wp);
+      const i16x4 hi = lds_read_tr16(wp + 4 * GN);
+      wa[ks][nb] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  for (int mt = stream; mt < Mt; mt += streams) {
+    lds_barrier();  // the previous tile's C staging is consumed
+#pragma unroll
+    for (int c = 0; c < MCH; ++c) {
+      const int idx = tid + NT * c;
+      *(i32x4*)&Ms[(idx / (PP_K / 8)) * PP_MP + (idx % (PP_K / 8)) * 8] = mr[c];
+    }
+    lds_barrier();
+    if (mt + streams < Mt) mload(mt + streams);
+
+    f32x16 acc[2][MB];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[nb][0] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < PP_K / 16; ++ks) {
+      const bf16x8 mb = *(const bf16x8*)&Ms[(wm * 32 + l32) * PP_MP + ks * 16 + hh * 8];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) acc[nb][0] = mfma32(wa[ks][nb], mb, acc[nb][0]);
+    }
+    lds_barrier();  // every wave is done with the m tile
+    {
+      const int tl = wm * 32 + l32;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 val;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) val[q] = (bf16)(acc[nb][0][g4 * 4 + q] * os);
+          *(bf16x4*)&Cs[tl * CP + wn * 64 + nb * 32 + 8 * g4 + 4 * hh] = val;
+        }
+      }
+    }
+    lds_barrier();
+    constexpr int CPT = 4;        // 16-byte chunks per token and head (dh = 32: 64 bytes)
+    constexpr int HPT = GN / 32;  // heads per channel tile
+    constexpr int NCHUNK = GM * HPT * CPT / NT;
+    static_assert(GM * HPT * CPT % NT == 0, "chunk/thread mismatch");
+#pragma unroll
+    for (int k = 0; k < NCHUNK; ++k) {
+      const int id = tid + NT * k;
+      const int hl = id / (GM * CPT);
+      const int rem = id % (GM * CPT);
+      const int tl = rem >> 2, e8 = rem & 3;
+      // tokens past M land past the plane and the buffer store drops them:
+      // every tile issues the same four stores, so the next tile's wait for
+      // its prefetched m rows can leave these stores in flight
+      const int tok = mt * GM + tl;
+      const int outer = tok / Linner, inner = tok % Linner;
+      const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * 32 + e8 * 8];
+      __builtin_amdgcn_raw_buffer_store_b128(
+          v, ors, (uint32_t)((((outer * a.H + h0 + hl) * Linner + inner) * a.dh + e8 * 8) * 2), 0, 0);
+    }
+  }
+}
+
 }  // namespace
 
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
@@ -223,7 +371,9 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   // 256 CUs at least four times over (N_res = 768 at 128 sequences: -5 %);
   // smaller grids keep the 128 x 128 tile at two workgroups per CU.
   const long long big_tiles = (long long)((M + 255) / 256) * (N / 256);
-  if (HD % 256 == 0 && big_tiles >= 4 * 256) {
+  if (a.Cm == PP_K && N % 128 == 0 && 32 % (N / 128) == 0) {
+    hipLaunchKernelGGL(evo_proj_persistent_kernel, dim3(PP_BLOCKS), dim3(512), 0, stream, a);
+  } else if (HD % 256 == 0 && big_tiles >= 4 * 256) {
     hipLaunchKernelGGL((evo_proj_kernel<256, 256, 512>), dim3(((M + 255) / 256) * (N / 256)), dim3(512), 0, stream, a);
   } else {
     hipLaunchKernelGGL((evo_proj_kernel<128, 128, 256>), dim3(((M + 127) / 128) * (N / 128)), dim3(256), 0, stream, a);

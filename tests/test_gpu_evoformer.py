@@ -46,6 +46,11 @@ def test_channel_and_head_counts(gpu_lib):
     _run(gpu_lib, 2, 64, Cm=64, H=4)
     _run(gpu_lib, 2, 64, Cm=320, H=12)
     _run(gpu_lib, 130, 40, Cm=256, H=8)  # token count not a multiple of the GEMM tile
+    # Cm = 256 takes the persistent projection when its 128-channel tiles
+    # (H of them at dh = 32) divide 32: 4 and 16 tiles here; 12 take the tiled form
+    _run(gpu_lib, 3, 100, Cm=256, H=4)
+    _run(gpu_lib, 2, 72, Cm=256, H=16)
+    _run(gpu_lib, 2, 72, Cm=256, H=12)
 
 
 def test_zero_gate_is_half(gpu_lib):
