@@ -518,11 +518,13 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     constexpr bool kOptimistic = SM == SM_NONE || kBias || SM == SM_GATE;
     constexpr int MODE = kOptimistic ? 0 : (SM == SM_SOFTCAP_FIXED || SM == SM_ALIBI) ? 2 : 1;
     bf16x8 pb[QB][NPS];
-    // Fixed-reference softcap: the wave raises its issue priority over its
-    // exponentials (its longest VALU stretch), so that stretch is not starved
-    // by the other wave of the SIMD (measured: 5-6 % faster unmasked at
-    // S = 1k-16k; the same region made vanilla and causal kernels slower)
-    if constexpr (SM == SM_SOFTCAP_FIXED) __builtin_amdgcn_s_setprio(1);
+    // Fixed-reference softcap and the bias tensor: the wave raises its issue
+    // priority over its exponentials (its longest VALU stretch), so that
+    // stretch is not starved by the other wave of the SIMD (measured: softcap
+    // 5-6 % faster unmasked at S = 1k-16k, bias tensor 4 %; the same region
+    // made vanilla, causal, ALiBi-causal and Evoformer kernels slower)
+    constexpr bool kPrioExp = SM == SM_SOFTCAP_FIXED || SM == SM_TBIAS;
+    if constexpr (kPrioExp) __builtin_amdgcn_s_setprio(1);
     if constexpr (kOptimistic) {
       // Optimistic: exponentiate against the current reference and keep the
       // result unless some exponential exceeds 2^64 (then the tile sum does)
@@ -591,7 +593,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
     }
 
-    if constexpr (SM == SM_SOFTCAP_FIXED) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kPrioExp) __builtin_amdgcn_s_setprio(0);
     // ---- O^T += V^T P^T; each transposed V fragment feeds every query block
     // all V^T operands of the tile are read before the first MFMA (the
     // scheduler would otherwise keep two in flight and wait on LDS eight times)
