@@ -69,6 +69,7 @@ class AvVariant(ctypes.Structure):
         ("bias_batch_stride", ctypes.c_int64),
         ("bias_head_stride", ctypes.c_int64),
         ("doc_order", ctypes.c_void_p),
+        ("doc_order_len", ctypes.c_int32),
     ]
 
 
@@ -146,19 +147,52 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, ndim):
+def _on_device(t) -> bool:
+    """True when ``t`` lives in HIP device memory (the kernels dereference its pointer)."""
+    return t.is_cuda
+
+
+def _need(t, name, dtype, ndim, device=None):
+    """Check a tensor argument: type, HIP device (the same one as ``device`` when
+    given), dtype, rank and contiguity."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
+    if not _on_device(t):
         raise ValueError(f"{name} must be on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _need_shape(t, name, dtype, shape, device):
+    """A caller-supplied output: exactly ``shape``, ``dtype``, contiguous, on ``device``.
+    The kernels write every element of that shape through the raw pointer."""
+    _need(t, name, dtype, len(shape), device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_workspace(ws, name, nbytes, device):
+    """A caller-supplied workspace: contiguous device memory of at least ``nbytes`` bytes."""
+    import torch
+
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _on_device(ws) or ws.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = ws.numel() * ws.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, {nbytes} needed")
+    return have
 
 
 def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alibi_max_bias=8.0,
@@ -172,7 +206,8 @@ def make_variant(score_mod="none", mask="none", *, scale=0.0, softcap=20.0, alib
                      float(alibi_max_bias), int(window), int(prefix_len),
                      None if doc_id is None else int(doc_id.data_ptr()), int(kv_group),
                      None if bias is None else int(bias.data_ptr()), int(bias_batch_stride), int(bias_head_stride),
-                     None if doc_order is None else int(doc_order.data_ptr()))
+                     None if doc_order is None else int(doc_order.data_ptr()),
+                     0 if doc_order is None else int(doc_order.numel()))
 
 
 def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0, alibi_max_bias=8.0,
@@ -188,25 +223,25 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
     import torch
 
     lib = load_library()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, 4)
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4, dev)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if doc_id is not None:
-        _need(doc_id, "doc_id", torch.int32, 2)
-        if tuple(doc_id.shape) != (B, Sq):
-            raise ValueError("doc_id must be [B, S]")
+        _need_shape(doc_id, "doc_id", torch.int32, (B, Sq), dev)
     if doc_order is not None:
-        _need(doc_order, "doc_order", torch.int32, 1)
+        _need(doc_order, "doc_order", torch.int32, 1, dev)
         if doc_order.numel() != attn_doc_order_len(B, Sq):
             raise ValueError("doc_order must come from attn_doc_order(doc_id) of this shape")
     bs = hs = 0
     if score_mod == "bias":
         if bias is None:
             raise ValueError("score_mod='bias' needs a bias tensor")
-        _need(bias, "bias", torch.bfloat16, 4)
+        _need(bias, "bias", torch.bfloat16, 4, dev)
         Bb, Hb = bias.shape[:2]
         if Bb not in (1, B) or Hb not in (1, Hq) or tuple(bias.shape[2:]) != (Sq, Skv):
             raise ValueError(f"bias must be [1 or B, 1 or Hq, Sq, Skv], got {tuple(bias.shape)}")
@@ -215,11 +250,13 @@ def attn_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
     elif bias is not None:
         raise ValueError("bias given without score_mod='bias'")
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, "out", torch.bfloat16, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        _need_shape(out, "out", torch.bfloat16, (B, Hq, Sq, D), dev)
+    if lse is not None:
+        _need_shape(lse, "lse", torch.float32, (B, Hq, Sq), dev)
+    elif return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
                        window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group, bias=bias,
                        bias_batch_stride=bs, bias_head_stride=hs, doc_order=doc_order)
@@ -247,7 +284,7 @@ def attn_doc_order(doc_id, out=None):
     if out is None:
         out = torch.empty((n,), dtype=torch.int32, device=doc_id.device)
     else:
-        _need(out, "out", torch.int32, 1)
+        _need_shape(out, "out", torch.int32, (n,), doc_id.device)
     rc = lib.attn_doc_order(doc_id.data_ptr(), B, S, out.data_ptr(), out.numel(), _stream_ptr(doc_id.device))
     _check(rc, "attn_doc_order")
     return out
@@ -266,28 +303,34 @@ def attn_decode_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softca
     import torch
 
     lib = load_library()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, 4)
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4, dev)
     B, Hq, Sq, D = q.shape
     Bk, Hkv, Skv, Dk = k.shape
     if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, "out", torch.bfloat16, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        _need_shape(out, "out", torch.bfloat16, (B, Hq, Sq, D), dev)
+    if lse is not None:
+        _need_shape(lse, "lse", torch.float32, (B, Hq, Sq), dev)
+    elif return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     need = lib.attn_decode_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) if Sq > 0 else 0
+    ws_bytes = 0
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
                        kv_group=kv_group)
     rc = lib.attn_decode_fwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                              None if lse is None else lse.data_ptr(),
                              None if workspace is None else workspace.data_ptr(),
-                             0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, Skv, D,
-                             _stream_ptr(q.device))
+                             ws_bytes, B, Hq, Hkv, Sq, Skv, D, _stream_ptr(dev))
     _check(rc, "attn_decode_fwd")
     return (out, lse) if return_lse else out
 
@@ -307,10 +350,11 @@ def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_m
 
     lib = load_library()
     _need(q, "q", torch.bfloat16, 4)
-    _need(k_cache, "k_cache", torch.bfloat16, 4)
-    _need(v_cache, "v_cache", torch.bfloat16, 4)
-    _need(block_table, "block_table", torch.int32, 2)
-    _need(seq_lens, "seq_lens", torch.int32, 1)
+    dev = q.device
+    _need(k_cache, "k_cache", torch.bfloat16, 4, dev)
+    _need(v_cache, "v_cache", torch.bfloat16, 4, dev)
+    _need(block_table, "block_table", torch.int32, 2, dev)
+    _need(seq_lens, "seq_lens", torch.int32, 1, dev)
     B, Hq, Sq, D = q.shape
     num_pages, Hkv, page_size, Dk = k_cache.shape
     if Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
@@ -319,22 +363,26 @@ def attn_decode_paged_fwd(q, k_cache, v_cache, block_table, seq_lens, *, score_m
         raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
     max_pages = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.bfloat16, device=dev)
     else:
-        _need(out, "out", torch.bfloat16, 4)
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+        _need_shape(out, "out", torch.bfloat16, (B, Hq, Sq, D), dev)
+    if lse is not None:
+        _need_shape(lse, "lse", torch.float32, (B, Hq, Sq), dev)
+    elif return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
     need = lib.attn_decode_paged_workspace_bytes(B, Hq, Hkv, Sq, D, page_size, max_pages) if Sq > 0 else 0
+    ws_bytes = 0
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
                        kv_group=kv_group)
     rc = lib.attn_decode_paged_fwd(ctypes.byref(var), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                    block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                    None if lse is None else lse.data_ptr(),
                                    None if workspace is None else workspace.data_ptr(),
-                                   0 if workspace is None else workspace.numel(), B, Hq, Hkv, Sq, D, page_size,
-                                   max_pages, num_pages, _stream_ptr(q.device))
+                                   ws_bytes, B, Hq, Hkv, Sq, D, page_size, max_pages, num_pages, _stream_ptr(dev))
     _check(rc, "attn_decode_paged_fwd")
     return (out, lse) if return_lse else out
 
@@ -350,24 +398,38 @@ def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, so
     import torch
 
     lib = load_library()
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
-        _need(t, n, torch.bfloat16, 4)
-    _need(lse, "lse", torch.float32, 3)
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, n, torch.bfloat16, 4, dev)
     B, Hq, Sq, D = q.shape
-    Hkv, Skv = k.shape[1], k.shape[2]
-    if tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Sq):
-        raise ValueError("dout must match q, lse must be [B, Hq, Sq]")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    Bk, Hkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout must match q")
+    _need_shape(lse, "lse", torch.float32, (B, Hq, Sq), dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    else:
+        _need_shape(dq, "dq", torch.bfloat16, (B, Hq, Sq, D), dev)
+    if dk is None:
+        dk = torch.empty_like(k)
+    else:
+        _need_shape(dk, "dk", torch.bfloat16, (B, Hkv, Skv, D), dev)
+    if dv is None:
+        dv = torch.empty_like(v)
+    else:
+        _need_shape(dv, "dv", torch.bfloat16, (B, Hkv, Skv, D), dev)
     need = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
                        kv_group=kv_group)
     rc = lib.attn_bwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                      workspace.numel(), B, Hq, Hkv, Sq, Skv, D, _stream_ptr(q.device))
+                      ws_bytes, B, Hq, Hkv, Sq, Skv, D, _stream_ptr(dev))
     _check(rc, "attn_bwd")
     return dq, dk, dv
 
@@ -377,14 +439,18 @@ def diff_attn_fwd(q, k, v, *, lam=0.8, scale=0.0, causal=True, out=None):
     import torch
 
     lib = load_library()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, 4)
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4, dev)
     B, H, S, D2 = q.shape
     if tuple(k.shape) != (B, H, S, D2) or v.shape[:3] != (B, H, S) or D2 % 2:
         raise ValueError("shape mismatch")
     Dv = v.shape[3]
     if out is None:
-        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=dev)
+    else:
+        _need_shape(out, "out", torch.bfloat16, (B, H, S, Dv), dev)
     rc = lib.diff_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, S, D2 // 2, Dv,
                            float(lam), float(scale or 0.0), int(bool(causal)), _stream_ptr(q.device))
     _check(rc, "diff_attn_fwd")
@@ -401,23 +467,23 @@ def diff_head_fwd(q, k, v, lambda_q1, lambda_k1, lambda_q2, lambda_k2, *, lambda
     import torch
 
     lib = load_library()
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, torch.bfloat16, 4)
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4, dev)
     B, H, S, D2 = q.shape
     if tuple(k.shape) != (B, H, S, D2) or v.shape[:3] != (B, H, S) or D2 % 2:
         raise ValueError("shape mismatch")
     Dv = v.shape[3]
     for t, n in ((lambda_q1, "lambda_q1"), (lambda_k1, "lambda_k1"), (lambda_q2, "lambda_q2"),
                  (lambda_k2, "lambda_k2")):
-        _need(t, n, torch.float32, 1)
-        if t.shape[0] != D2 // 2 or t.device != q.device:
-            raise ValueError(f"{n} must be [Dh] on the device of q")
+        _need_shape(t, n, torch.float32, (D2 // 2,), dev)
     if gamma is not None:
-        _need(gamma, "gamma", torch.float32, 1)
-        if gamma.shape[0] != Dv or gamma.device != q.device:
-            raise ValueError("gamma must be [Dv] on the device of q")
+        _need_shape(gamma, "gamma", torch.float32, (Dv,), dev)
     if out is None:
-        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((B, H, S, Dv), dtype=torch.bfloat16, device=dev)
+    else:
+        _need_shape(out, "out", torch.bfloat16, (B, H, S, Dv), dev)
     rc = lib.diff_head_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), lambda_q1.data_ptr(), lambda_k1.data_ptr(),
                            lambda_q2.data_ptr(), lambda_k2.data_ptr(), None if gamma is None else gamma.data_ptr(),
                            out.data_ptr(), B, H, S, D2 // 2, Dv, float(lambda_init), float(eps), float(scale or 0.0),
@@ -440,22 +506,21 @@ def evoformer_gated_attn_fwd(m, wq, wk, wv, wg, bias, *, H, dh, scale=0.0, works
 
     lib = load_library()
     _need(m, "m", torch.bfloat16, 3)
-    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
-        _need(t, n, torch.bfloat16, 2)
-    _need(bias, "bias", torch.bfloat16, 3)
+    dev = m.device
     Ns, Nr, Cm = m.shape
-    for t in (wq, wk, wv, wg):
-        if tuple(t.shape) != (Cm, H * dh):
-            raise ValueError("projection weights must be [Cm, H*dh]")
-    if tuple(bias.shape) != (H, Nr, Nr):
-        raise ValueError("bias must be [H, Nr, Nr]")
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
+        _need_shape(t, n, torch.bfloat16, (Cm, H * dh), dev)
+    _need_shape(bias, "bias", torch.bfloat16, (H, Nr, Nr), dev)
     need = evoformer_workspace_bytes(Ns, Nr, H, dh)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=m.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     if out is None:
-        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=m.device)
+        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=dev)
+    else:
+        _need_shape(out, "out", torch.bfloat16, (Ns, Nr, H * dh), dev)
     rc = lib.evoformer_gated_attn_fwd(m.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wg.data_ptr(),
-                                      bias.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      bias.data_ptr(), out.data_ptr(), workspace.data_ptr(), ws_bytes,
                                       Ns, Nr, Cm, H, dh, float(scale or 0.0), _stream_ptr(m.device))
     _check(rc, "evoformer_gated_attn_fwd")
     return out
@@ -472,19 +537,20 @@ def evoformer_col_gated_attn_fwd(m, wq, wk, wv, wg, *, H, dh, scale=0.0, workspa
 
     lib = load_library()
     _need(m, "m", torch.bfloat16, 3)
-    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
-        _need(t, n, torch.bfloat16, 2)
+    dev = m.device
     Ns, Nr, Cm = m.shape
-    for t in (wq, wk, wv, wg):
-        if tuple(t.shape) != (Cm, H * dh):
-            raise ValueError("projection weights must be [Cm, H*dh]")
+    for t, n in ((wq, "wq"), (wk, "wk"), (wv, "wv"), (wg, "wg")):
+        _need_shape(t, n, torch.bfloat16, (Cm, H * dh), dev)
     need = evoformer_workspace_bytes(Ns, Nr, H, dh)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=m.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     if out is None:
-        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=m.device)
+        out = torch.empty((Ns, Nr, H * dh), dtype=torch.bfloat16, device=dev)
+    else:
+        _need_shape(out, "out", torch.bfloat16, (Ns, Nr, H * dh), dev)
     rc = lib.evoformer_col_gated_attn_fwd(m.data_ptr(), wq.data_ptr(), wk.data_ptr(), wv.data_ptr(), wg.data_ptr(),
-                                          out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                          out.data_ptr(), workspace.data_ptr(), ws_bytes,
                                           Ns, Nr, Cm, H, dh, float(scale or 0.0), _stream_ptr(m.device))
     _check(rc, "evoformer_col_gated_attn_fwd")
     return out

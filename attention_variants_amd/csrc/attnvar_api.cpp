@@ -113,6 +113,13 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
   if (var->doc_order != nullptr && var->mask != AV_MASK_DOCUMENT) return AV_ERR_PARAM;
   if (var->doc_order != nullptr && !aligned(var->doc_order, 4)) return AV_ERR_ALIGN;
+  if (var->doc_order != nullptr) {
+    // the kernel reads entry blockIdx.x / Hq < B * ceil(Sq / 128): the order
+    // must be the one attn_doc_order writes for this B and Sq
+    const int n = attn_doc_order_len(B, Sq);
+    if (n < 0) return n;
+    if (var->doc_order_len != n) return AV_ERR_PARAM;
+  }
   // bias rows are read 8 bytes at a time when Skv % 4 == 0: every slice must
   // then start on an 8-byte boundary
   if (tbias && (!aligned(var->bias, 8) ||
@@ -347,6 +354,11 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
         return AV_ERR_HIP;
     }
     return AV_OK;
+  }
+  if (Skv == 0) {
+    // no key (mask none only: a mask needs Sq == Skv): the output is the
+    // constant zero row, so every query gets a zero gradient
+    return hip_status(av::launch_zero_fill(dq, (size_t)B * Hq * Sq * D * 2, stream));
   }
   const size_t need = (size_t)B * Hq * Sq * 8;
   if (workspace == nullptr || workspace_bytes < need) return AV_ERR_WORKSPACE;

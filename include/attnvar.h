@@ -99,11 +99,17 @@ typedef struct {
   int64_t bias_batch_stride;
   int64_t bias_head_stride;
   /* AV_MASK_DOCUMENT, optional (NULL = natural order): device int32 order of
-   * the query tiles written by attn_doc_order for the same doc_id, B and S,
-   * holding attn_doc_order_len(B, S) entries.  It changes only the order in
-   * which attn_fwd visits its work, never a result bit.  Non-NULL with any
-   * other mask is AV_ERR_PARAM; 4-byte aligned.  Read by attn_fwd only. */
+   * the query tiles written by attn_doc_order for the same doc_id, B and S.
+   * It changes only the order in which attn_fwd visits its work, never a
+   * result bit.  Non-NULL with any other mask is AV_ERR_PARAM; 4-byte
+   * aligned.  Read by attn_fwd only. */
   const int32_t* doc_order;
+  /* Entries the doc_order buffer holds.  attn_fwd reads exactly
+   * n = attn_doc_order_len(B, Sq) of them; doc_order_len != n is
+   * AV_ERR_PARAM (an order built for another shape), and a shape for which
+   * attn_doc_order_len fails is that function's error.  Ignored when
+   * doc_order is NULL. */
+  int32_t doc_order_len;
 } av_variant;
 
 /* Fused attention forward, MHA and GQA.
@@ -272,7 +278,7 @@ int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, 
 const char* av_status_string(int status);
 
 /* ABI version of this header; bumped when a signature or struct changes. */
-#define AV_ABI_VERSION 3
+#define AV_ABI_VERSION 4
 int av_abi_version(void);
 
 #ifdef __cplusplus

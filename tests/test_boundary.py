@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.av_abi_version() == 3
+    assert lib.av_abi_version() == 4
     for code, name in av.STATUS.items():
         assert lib.av_status_string(code).decode().startswith(name)
     assert lib.av_status_string(12345).decode() == "unknown av_status"
@@ -149,6 +149,15 @@ def test_doc_order_rejections(lib):
     v.doc_id = 0x90000
     v.doc_order = 0x80002
     assert _attn(lib, v) == -4
+    # the order's length must be attn_doc_order_len(B, Sq) of this call
+    v.doc_order = 0x80000
+    for n in (0, 1, 3, 5, 1 << 20):
+        v.doc_order_len = n
+        assert _attn(lib, v, B=2, Sq=256, Skv=256) == -7, n
+    v.doc_order_len = 2
+    assert _attn(lib, v, B=1, Sq=257, Skv=257) == -7      # 3 tiles of 128 rows
+    v.doc_order_len = 4
+    assert _attn(lib, v, B=2, Sq=256, Skv=256, Hq=2, Hkv=4) == -2  # shape errors come first
     assert av.attn_doc_order_len(4, 4096) == 128
     with pytest.raises(RuntimeError):
         av.attn_doc_order_len(1, 16384 * 128 + 1)
@@ -310,6 +319,90 @@ def test_evoformer_column_rejections(lib):
     assert call(ws=None) == -5
     assert call(wsb=1) == -5
     assert call(ws=0x100000 + 128) == -4
+
+
+class _FakeDevice:
+    """Lets the binding's checks accept host tensors, so that a wrong caller
+    buffer can be shown to raise before anything reaches the library (with a
+    host pointer the library call itself would fail with a HIP error)."""
+
+    def __init__(self, monkeypatch):
+        monkeypatch.setattr(av, "_on_device", lambda t: True)
+
+
+def _bf(*shape):
+    import torch
+
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_wrong_output_buffers(monkeypatch):
+    import torch
+
+    _FakeDevice(monkeypatch)
+    q, kv = _bf(2, 4, 8, 64), _bf(2, 2, 8, 64)
+    f32 = torch.float32
+    bad = [
+        dict(out=_bf(2, 4, 8, 32)),                      # wrong shape
+        dict(out=_bf(2, 4, 7, 64)),
+        dict(out=torch.zeros(2, 4, 8, 64)),              # wrong dtype (TypeError)
+        dict(lse=torch.zeros(2, 4, 7, dtype=f32)),
+        dict(lse=torch.zeros(2, 4, 8, 1, dtype=f32)),
+        dict(out=_bf(2, 4, 64, 8).transpose(2, 3)),      # not contiguous
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            av.attn_fwd(q, kv, kv, **kw)
+    with pytest.raises(ValueError):
+        av.attn_fwd(q, kv, _bf(2, 2, 7, 64))             # v shorter than k
+    with pytest.raises(ValueError):
+        av.attn_fwd(q, kv, kv, mask="document", doc_id=torch.zeros(2, 7, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        av.attn_decode_fwd(q, kv, kv, out=_bf(2, 4, 8, 63))
+    with pytest.raises(ValueError):
+        av.attn_decode_fwd(q, kv, kv, lse=torch.zeros(2, 4, 9, dtype=f32))
+
+
+def test_binding_rejects_wrong_backward_buffers(monkeypatch):
+    import torch
+
+    _FakeDevice(monkeypatch)
+    q, kv = _bf(1, 4, 16, 64), _bf(1, 2, 16, 64)
+    lse = torch.zeros(1, 4, 16)
+    for kw in (dict(dq=_bf(1, 4, 15, 64)), dict(dk=_bf(1, 4, 16, 64)), dict(dv=_bf(1, 2, 16, 32)),
+               dict(workspace=torch.zeros(8, dtype=torch.uint8))):
+        with pytest.raises(ValueError):
+            av.attn_bwd(q, kv, kv, q, lse, **kw)
+    with pytest.raises(ValueError):
+        av.attn_bwd(q, kv, _bf(1, 2, 15, 64), q, lse)  # v and k disagree
+    with pytest.raises(ValueError):
+        av.attn_bwd(q, kv, _bf(1, 1, 16, 64), q, lse)
+    with pytest.raises(ValueError):
+        av.attn_bwd(q, kv, kv, q, torch.zeros(1, 4, 17))
+
+
+def test_binding_rejects_wrong_diff_and_evoformer_buffers(monkeypatch):
+    import torch
+
+    _FakeDevice(monkeypatch)
+    q, v = _bf(1, 2, 8, 128), _bf(1, 2, 8, 128)
+    with pytest.raises(ValueError):
+        av.diff_attn_fwd(q, q, v, out=_bf(1, 2, 8, 64))
+    lam = torch.zeros(64)
+    with pytest.raises(ValueError):
+        av.diff_head_fwd(q, q, v, lam, lam, lam, lam, lambda_init=0.2, out=_bf(1, 2, 9, 128))
+    with pytest.raises(ValueError):
+        av.diff_head_fwd(q, q, v, lam, lam, lam, torch.zeros(32), lambda_init=0.2)
+    m, w, b = _bf(2, 16, 64), _bf(64, 128), _bf(4, 16, 16)
+    with pytest.raises(ValueError):
+        av.evoformer_gated_attn_fwd(m, w, w, w, w, b, H=4, dh=32, out=_bf(2, 16, 64))
+    with pytest.raises(ValueError):
+        av.evoformer_gated_attn_fwd(m, w, w, w, w, b, H=4, dh=32,
+                                    workspace=torch.zeros(100, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        av.evoformer_gated_attn_fwd(m, w, w, w, _bf(64, 64), b, H=4, dh=32)
+    with pytest.raises(ValueError):
+        av.evoformer_col_gated_attn_fwd(m, w, w, w, w, H=4, dh=32, out=_bf(2, 15, 128))
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -218,17 +218,45 @@ def test_score_mod_sweep_S4096(gpu_lib, score_mod):
     _run(gpu_lib, 16384 // S, 16, 16, S, 64, score_mod, "none", rows=rows, rms_check=True)
 
 
+def _must_rows(S, B, mask):
+    """Rows every sampled check includes beyond the tile edges: the PrefixLM
+    prefix edge, the sliding window's first full row, every document edge."""
+    must = [S // 4 - 1, S // 4, S // 4 + 1]
+    if mask == "sliding_window":
+        must += [255, 256, 257]
+    if mask == "document":
+        for b_lens in wi.doc_lengths(4, B, S):
+            must += list(np.cumsum(b_lens)[:-1]) + list(np.cumsum(b_lens)[:-1] - 1)
+    return must
+
+
 @pytest.mark.parametrize("mask", MASKS[1:])
 @pytest.mark.parametrize("Hkv", [16, 2])
 def test_mask_sweep_S4096(gpu_lib, mask, Hkv):
     S = 4096
     B = 16384 // S
-    must = [S // 4 - 1, S // 4, S // 4 + 1]
-    if mask == "document":
-        for b_lens in wi.doc_lengths(4, B, S):
-            must += list(np.cumsum(b_lens)[:-1]) + list(np.cumsum(b_lens)[:-1] - 1)
-    rows = sample_rows_at_least(S, 512, seed=2, must=must)
+    rows = sample_rows_at_least(S, 512, seed=2, must=_must_rows(S, B, mask))
     _run(gpu_lib, B, 16, Hkv, S, 64, "none", mask, rows=rows, rms_check=True)
+
+
+@pytest.mark.parametrize("score_mod,mask,Hkv", BENCH_VARIANTS)
+def test_benchmark_shapes_S8192(gpu_lib, score_mod, mask, Hkv):
+    """S = 8k, B = 2 (16k tokens, 16 query heads): at least 512 sampled rows
+    per head of both batch entries, tile, prefix and document edges included."""
+    S = 8192
+    B = 16384 // S
+    rows = sample_rows_at_least(S, 512, tiles=(128,), seed=6, must=_must_rows(S, B, mask))
+    _run(gpu_lib, B, 16, Hkv, S, 64, score_mod, mask, rows=rows, rms_check=True)
+
+
+@pytest.mark.parametrize("mask,Hkv", [("causal", 16), ("causal", 2), ("sliding_window", 16), ("sliding_window", 2),
+                                      ("prefix_lm", 16), ("prefix_lm", 2), ("document", 16)])
+def test_masks_S16384(gpu_lib, mask, Hkv):
+    """The masked benchmark variants at S = 16k, B = 1 not covered by the
+    sweep-extremes test, sampled as at S = 8k."""
+    S = 16384
+    rows = sample_rows_at_least(S, 512, tiles=(128,), seed=7, must=_must_rows(S, 1, mask))
+    _run(gpu_lib, 1, 16, Hkv, S, 64, "none", mask, rows=rows, rms_check=True)
 
 
 @pytest.mark.parametrize("S", [512, 16384])

@@ -77,3 +77,15 @@ def test_bwd_benchmark_shape(gpu_lib, score_mod, mask):
     assert_close(dq[sl].float().cpu().numpy(), rq, what + " dq")
     assert_close(dk[sl].float().cpu().numpy(), rk, what + " dk")
     assert_close(dv[sl].float().cpu().numpy(), rv, what + " dv")
+
+
+def test_bwd_no_keys_gives_zero_dq(gpu_lib):
+    """Skv = 0: the output is the constant zero row, so dq is zero (and nothing else is written)."""
+    q = torch.randn(1, 2, 5, 64, device="cuda").to(torch.bfloat16)
+    kv = torch.zeros(1, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    out, lse = gpu_lib.attn_fwd(q, kv, kv, return_lse=True)
+    dq = torch.full_like(q, 3.0)
+    dq, dk, dv = gpu_lib.attn_bwd(q, kv, kv, torch.ones_like(q), lse, dq=dq)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0).item()
+    assert dk.numel() == 0 and dv.numel() == 0

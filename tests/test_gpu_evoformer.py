@@ -70,15 +70,18 @@ def test_workspace_too_small_is_rejected(gpu_lib):
     x = wi.evoformer_inputs(2, 32, 64, 4, 32)
     t = {n: to_dev(x[n]) for n in x}
     ws = torch.empty(100, dtype=torch.uint8, device="cuda")
-    with pytest.raises(RuntimeError, match="WORKSPACE"):
+    with pytest.raises(ValueError, match="bytes"):
         gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=4, dh=32,
                                          workspace=ws)
 
 
 @pytest.mark.parametrize("Nr", [256, 384, 768])
 def test_benchmark_shapes(gpu_lib, Nr):
-    seqs = np.array([0, 1, 64, 127])
+    # 20 sequences spread over the grid (every 8th, the ends and random ones)
+    # and about 46 residues per sequence, tile edges included
     rng = np.random.default_rng(7)
+    seqs = np.unique(np.concatenate([np.arange(0, 128, 8), [1, 127], rng.integers(0, 128, 4)]))
+    assert len(seqs) >= 16
     rows = np.unique(np.concatenate([[0, 1, Nr - 1, 127, 128, Nr // 2], rng.integers(0, Nr, 40)]))
     _run(gpu_lib, 128, Nr, seqs=seqs, rows=rows)
 
