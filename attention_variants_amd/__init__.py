@@ -38,6 +38,7 @@ EXPORTED = (
     "attn_doc_order",
     "attn_decode_workspace_bytes",
     "attn_decode_fwd",
+    "attn_decode_fwd_noalloc",
     "attn_decode_paged_workspace_bytes",
     "attn_decode_paged_fwd",
     "attn_bwd_workspace_bytes",
@@ -100,6 +101,9 @@ def load_library(path: str | None = None):
     lib.attn_decode_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                     _i, _i, _i, _i, _i, _i, _vp]
     lib.attn_decode_fwd.restype = _i
+    lib.attn_decode_fwd_noalloc.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp,
+                                            _i, _i, _i, _i, _i, _i, _vp]
+    lib.attn_decode_fwd_noalloc.restype = _i
     lib.attn_decode_paged_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
     lib.attn_decode_paged_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_decode_paged_fwd.argtypes = [ctypes.POINTER(AvVariant), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -333,6 +337,35 @@ def attn_decode_fwd(q, k, v, *, score_mod="none", mask="none", scale=0.0, softca
                              ws_bytes, B, Hq, Hkv, Sq, Skv, D, _stream_ptr(dev))
     _check(rc, "attn_decode_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_decode_fwd_noalloc(q, k, v, out, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
+                            alibi_max_bias=8.0, kv_group=0, lse=None):
+    """attn_decode_fwd without a workspace: the library keeps the split-KV
+    partials in its static per-GPU array, so the call allocates nothing.  The
+    caller passes ``out`` (and optionally ``lse``); calls that overlap on one
+    GPU race."""
+    import torch
+
+    lib = load_library()
+    _need(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, torch.bfloat16, 4, dev)
+    B, Hq, Sq, D = q.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    _need_shape(out, "out", torch.bfloat16, (B, Hq, Sq, D), dev)
+    if lse is not None:
+        _need_shape(lse, "lse", torch.float32, (B, Hq, Sq), dev)
+    var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
+                       kv_group=kv_group)
+    rc = lib.attn_decode_fwd_noalloc(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                     None if lse is None else lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                                     _stream_ptr(dev))
+    _check(rc, "attn_decode_fwd_noalloc")
+    return out
 
 
 def attn_decode_paged_workspace_bytes(B, Hq, Hkv, Sq, D, page_size, max_pages) -> int:

@@ -25,6 +25,7 @@
 //    the online softmax), one workgroup per output row.
 
 #include <algorithm>
+#include <mutex>
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
@@ -43,6 +44,8 @@ constexpr int ROWS = 32; // query rows per workgroup (one MFMA block)
 #endif
 constexpr int kDecodeTargetWG = AV_DECODE_TARGET_WG;
 constexpr int kDecodeMinTiles = AV_DECODE_MIN_TILES;
+static_assert((size_t)2 * kDecodeTargetWG * 32 * (64 + 2) * 4 <= kDecodeScratchBytes,
+              "the allocation-free decode scratch must hold the partials of every plan");
 
 // (the paged form holds 64-bit row addresses: two waves per SIMD instead of three)
 template <int D, int SM, bool CAUSAL, bool PAGED>
@@ -369,6 +372,40 @@ size_t decode_workspace_bytes(int B, int Hkv, int Skv, int D) {
   const DecodePlan p = decode_plan(B, Hkv, Skv);
   if (p.NS == 1) return 0;
   return (size_t)B * Hkv * p.NS * 32 * ((size_t)D + 2) * 4;
+}
+
+// Split-KV partials of the allocation-free decode entry point, one copy per
+// GPU, held until the process ends.  The plan splits the keys only while
+// B * Hkv < kDecodeTargetWG, and then into at most ceil(target / (B * Hkv))
+// splits, so B * Hkv * NS < 2 * kDecodeTargetWG: the partial state of any
+// plan at D = 64 fits kDecodeScratchBytes (8.25 MiB at the default target).
+// Every call overwrites the rows it later reads, so nothing needs clearing;
+// calls that overlap on one GPU share these bytes and race.
+__device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // the host-side name of the array is a stand-in, not a device address:
+    // this device's copy lives at the address the runtime reports
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream) {

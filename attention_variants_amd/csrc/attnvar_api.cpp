@@ -193,9 +193,15 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int 
   return av::decode_workspace_bytes(B, Hkv, Skv, D);
 }
 
-int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse,
-                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
-                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and argument block of the dense decode forms; `need` receives
+// the split-KV partials' byte count (0 when the plan does not split).
+int decode_prepare(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int Hq, int Hkv, int Sq, int Skv, int D, av::DecodeArgs& a, size_t& need) {
+  need = 0;
   if (var == nullptr) return AV_ERR_NULL;
   if ((Sq > 0 && (q == nullptr || out == nullptr)) || (Skv > 0 && (k == nullptr || v == nullptr)))
     return AV_ERR_NULL;
@@ -217,18 +223,14 @@ int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const v
   const av::DecodePlan plan = av::decode_plan(B, Hkv, Skv);
   const int64_t total = (int64_t)B * Hkv * plan.NS;
   if (total > INT32_MAX || (int64_t)B * Hkv * 32 > INT32_MAX) return AV_ERR_TOO_LARGE;
-  const size_t need = av::decode_workspace_bytes(B, Hkv, Skv, D);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return AV_ERR_WORKSPACE;
-  if (need > 0 && !aligned(workspace, 16)) return AV_ERR_ALIGN;
+  need = av::decode_workspace_bytes(B, Hkv, Skv, D);
 
-  av::DecodeArgs a{};
+  a = av::DecodeArgs{};
   a.q = q;
   a.k = k;
   a.v = v;
   a.o = out;
   a.lse = lse;
-  a.ws_o = need > 0 ? (float*)workspace : nullptr;
-  a.ws_ml = need > 0 ? (float*)workspace + (size_t)B * Hkv * plan.NS * 32 * D : nullptr;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -244,6 +246,42 @@ int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const v
   a.alibi_max_bias = var->alibi_max_bias;
   a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
   a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
+  return AV_OK;
+}
+
+// partial O [B*Hkv, NS, 32, D] fp32, then (m, l) [B*Hkv, NS, 32, 2] fp32
+void decode_set_workspace(av::DecodeArgs& a, void* ws, size_t need, int D) {
+  a.ws_o = need > 0 ? (float*)ws : nullptr;
+  a.ws_ml = need > 0 ? (float*)ws + (size_t)a.B * a.Hkv * a.NS * 32 * D : nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse,
+                    void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
+                    hipStream_t stream) {
+  av::DecodeArgs a{};
+  size_t need = 0;
+  const int rc = decode_prepare(var, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, a, need);
+  if (rc != AV_OK || Sq == 0) return rc;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return AV_ERR_WORKSPACE;
+  if (need > 0 && !aligned(workspace, 16)) return AV_ERR_ALIGN;
+  decode_set_workspace(a, workspace, need, D);
+  return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
+}
+
+int attn_decode_fwd_noalloc(const av_variant* var, const void* q, const void* k, const void* v, void* out,
+                            float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
+  av::DecodeArgs a{};
+  size_t need = 0;
+  const int rc = decode_prepare(var, q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, a, need);
+  if (rc != AV_OK || Sq == 0) return rc;
+  if (need > av::kDecodeScratchBytes) return AV_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0 && av::decode_scratch(&ws) != hipSuccess) return AV_ERR_HIP;
+  decode_set_workspace(a, ws, need, D);
   return hip_status(av::launch_attn_decode(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
 }
 

@@ -109,6 +109,13 @@ struct DecodePlan {
 };
 DecodePlan decode_plan(int B, int Hkv, int Skv);
 size_t decode_workspace_bytes(int B, int Hkv, int Skv, int D);
+// Bound of decode_workspace_bytes over every plan at D = 64 (the plan splits
+// only while B * Hkv < 512 and keeps B * Hkv * NS < 1024), and the per-device
+// address of the static array of that size that the allocation-free decode
+// entry point uses in place of a caller workspace (looked up once per device,
+// on the current device).
+constexpr size_t kDecodeScratchBytes = (size_t)1024 * 32 * (64 + 2) * 4;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream);
 
 // Attention backward (D = 64; masks none / causal).

@@ -170,6 +170,22 @@ int attn_decode_fwd(const av_variant* variant, const void* q, const void* k, con
                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Sq, int Skv, int D,
                     hipStream_t stream);
 
+/* attn_decode_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments, limits, kernels and results, with no
+ * workspace argument.  The split-KV partials go to a static device array of
+ * 8650752 bytes (8.25 MiB) that every GPU the library runs on holds until
+ * the process ends; the call itself allocates nothing.  Every plan of the supported shapes fits (the keys are split only
+ * while B * Hkv < 512, into fewer than 1024 (b, KV head, split) units of
+ * 32 x 66 fp32 values); a plan that would not returns AV_ERR_TOO_LARGE.  The
+ * call runs on the current device (the stream must belong to it); the first
+ * call on a device looks the array's address up there (AV_ERR_HIP if that
+ * fails).  All calls on one GPU share the array: calls that can overlap on
+ * one GPU (different streams, or graphs replayed concurrently) race and
+ * must be ordered by the caller. */
+int attn_decode_fwd_noalloc(const av_variant* variant, const void* q, const void* k, const void* v, void* out,
+                            float* lse, int B, int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream);
+
 /* Decoding against a paged key/value cache (the vLLM-style serving layout of
  * the pages' end-to-end workload; same operation and limits as
  * attn_decode_fwd, with per-sequence key counts):

@@ -426,3 +426,14 @@ def test_binding_has_every_exported_function():
         if name.startswith("av_"):
             continue
         assert callable(getattr(av, name, None)), name
+
+
+def test_decode_partials_fit_the_static_array(lib):
+    """Every decode plan's split-KV partials fit the 8650752-byte array of the
+    allocation-free entry point: exhaustive over 1..1100 (batch, KV head)
+    units at key counts from one tile to 2^20 keys."""
+    worst = 0
+    for units in range(1, 1101):
+        for skv in (1, 64 * 4, 64 * 4 * 7 + 1, 4096, 16384, 100003, 1 << 20):
+            worst = max(worst, lib.attn_decode_workspace_bytes(1, units, units, 1, skv, 64))
+    assert 0 < worst <= 8650752
