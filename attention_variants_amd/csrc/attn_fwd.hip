@@ -58,11 +58,12 @@ constexpr int BN = 64;   // keys per KV tile
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 
 // Waves per SIMD each instantiation's register budget is sized for: two
-// with two query blocks per wave, D = 128 or the bias tensor at D = 64 (its
-// prefetched bias tile does not fit a third wave's budget), three otherwise.
+// with two query blocks per wave, D = 128 or a bias tile at D = 64 (the
+// prefetched bias of the bias tensor or the Evoformer pair bias does not fit
+// a third wave's budget), three otherwise.
 template <int D, int SM, int MK>
 constexpr int min_waves() {
-  return attn_qb(D, SM, MK) == 2 || D == 128 || (SM == SM_TBIAS && D == 64) ? 2 : 3;
+  return attn_qb(D, SM, MK) == 2 || D == 128 || ((SM == SM_TBIAS || SM == SM_BIAS) && D == 64) ? 2 : 3;
 }
 
 template <int D, int SM, int MK>
@@ -756,7 +757,8 @@ hipError_t launch_sm(const AttnArgs& a, int sm, int mask, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_evo_attention(const AttnArgs& a, int col, hipStream_t stream) {
+hipError_t launch_evo_attention(const AttnArgs& a, int D, int col, hipStream_t stream) {
+  if (D == 64) return col ? launch_one<64, SM_GATE, MK_NONE>(a, stream) : launch_one<64, SM_BIAS, MK_NONE>(a, stream);
   return col ? launch_one<32, SM_GATE, MK_NONE>(a, stream) : launch_one<32, SM_BIAS, MK_NONE>(a, stream);
 }
 

@@ -25,7 +25,7 @@ int diff_launch(av::DiffArgs& a, const void* q, const void* k, const void* v, vo
                 int Dh, int Dv, float scale, int causal, hipStream_t stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return AV_ERR_NULL;
   if (B <= 0 || H <= 0 || S < 0 || Dh <= 0 || Dv <= 0) return AV_ERR_SHAPE;
-  if (Dh != 64 || (Dv != 64 && Dv != 128)) return AV_ERR_UNSUPPORTED;
+  if ((Dh != 32 && Dh != 64) || (Dv != 64 && Dv != 128)) return AV_ERR_UNSUPPORTED;
   if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
   if ((uint64_t)(S + av::kAttnBM) * 2 * Dh * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
@@ -46,7 +46,7 @@ int diff_launch(av::DiffArgs& a, const void* q, const void* k, const void* v, vo
   const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
   a.c = (float)(sc * kLog2e);
   a.causal = causal != 0;
-  return hip_status(av::launch_diff_attn_fwd(a, Dv, stream));
+  return hip_status(av::launch_diff_attn_fwd(a, Dh, Dv, stream));
 }
 
 }  // namespace
@@ -475,7 +475,7 @@ int evoformer_launch(const void* m, const void* wq, const void* wk, const void* 
       (!col && bias == nullptr))
     return AV_ERR_NULL;
   if (Ns <= 0 || Nr <= 0 || Cm <= 0 || H <= 0 || dh <= 0) return AV_ERR_SHAPE;
-  if (dh != 32 || Cm % 64 != 0 || (H * dh) % 128 != 0) return AV_ERR_UNSUPPORTED;
+  if ((dh != 32 && dh != 64) || Cm % 64 != 0 || (H * dh) % 128 != 0) return AV_ERR_UNSUPPORTED;
   if (!(isfinite(scale) && scale >= 0.f)) return AV_ERR_PARAM;
   if (!aligned(m, 16) || !aligned(wq, 16) || !aligned(wk, 16) || !aligned(wv, 16) || !aligned(wg, 16) ||
       (!col && !aligned(bias, 16)) || !aligned(out, 16))

@@ -57,10 +57,12 @@ struct AttnArgs {
 // Evoformer shapes: short rows, where more and smaller workgroups hide the
 // load latency better), for the sliding window and document masks, whose
 // short per-row key ranges favour more, smaller workgroups, and for the bias
-// tensor (its prefetched bias tile takes the registers of a second block).
+// tensor and the Evoformer forms (their staged bias tile or gate
+// pre-activations take the registers of a second block).
 constexpr int kAttnBM = 128;
 constexpr int attn_qb(int D, int sm, int mask) {
-  return (D == 64 && mask != MK_WINDOW && mask != MK_DOC && sm != SM_TBIAS) ? 2 : 1;
+  return (D == 64 && mask != MK_WINDOW && mask != MK_DOC && sm != SM_TBIAS && sm != SM_BIAS && sm != SM_GATE) ? 2
+                                                                                                             : 1;
 }
 constexpr int attn_bm(int D, int sm, int mask) { return 4 * 32 * attn_qb(D, sm, mask); }
 constexpr int kAttnBMMax = 256;
@@ -77,9 +79,9 @@ static_assert(attn_bm(32, SM_NONE, MK_DOC) == kDocTileM && attn_bm(128, SM_NONE,
 hipError_t launch_doc_order(const int* doc, int B, int S, int* order, hipStream_t stream);
 
 hipError_t launch_attn_fwd(const AttnArgs& a, int D, int score_mod, int mask, hipStream_t stream);
-// Evoformer gated attention over the projected workspace (D = 32): row-wise
-// (SM_BIAS) or column-wise (SM_GATE).
-hipError_t launch_evo_attention(const AttnArgs& a, int col, hipStream_t stream);
+// Evoformer gated attention over the projected workspace (D = head width, 32
+// or 64): row-wise (SM_BIAS) or column-wise (SM_GATE).
+hipError_t launch_evo_attention(const AttnArgs& a, int D, int col, hipStream_t stream);
 
 // Decoding / short-query attention (split-KV): the Sq queries are the last
 // Sq positions of the keys; one workgroup per (batch, KV head, key split)
@@ -154,7 +156,7 @@ struct DiffArgs {
   float lambda;
   int causal;
   // full head form (lam_q1 != nullptr): lambda = exp(lq1.lk1) - exp(lq2.lk2)
-  // + lambda_init computed in the kernel from four fp32 [64] vectors, then
+  // + lambda_init computed in the kernel from four fp32 [Dh] vectors, then
   // the per-row RMS norm with the fp32 [Dv] weight gamma (nullable = ones)
   // and the (1 - lambda_init) factor
   const float* lam_q1;
@@ -164,7 +166,7 @@ struct DiffArgs {
   const float* gamma;
   float lambda_init, eps;
 };
-hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dv, hipStream_t stream);
+hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dh, int Dv, hipStream_t stream);
 
 struct EvoArgs {
   const void* m;

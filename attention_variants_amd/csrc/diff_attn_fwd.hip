@@ -5,8 +5,9 @@
 // PyTorch Compiler Extensions to Accelerate Attention Variants", sections
 // "Background and motivation" and "Evaluation: complex attention variants")
 // but do not define it.  The reading implemented: Q and K rows hold two
-// halves of width 64; each half yields its own softmax with scale 1/sqrt(64)
-// (causal when asked); out = (P1 - lambda * P2) V with V of width Dv.
+// halves of width Dh (64 for the 16 heads x 128 shape, 32 for 32 heads x 64);
+// each half yields its own softmax with scale 1/sqrt(Dh) (causal when asked);
+// out = (P1 - lambda * P2) V with V of width Dv.
 //
 // Kernel shape: the fused attention kernel's skeleton with two score tiles
 // and two online-softmax states per query row.  One workgroup = 4 waves =
@@ -19,7 +20,7 @@
 // published Differential Transformer defines it (Ye et al., 2024; the pages
 // name DiffTransformer under related work, talk notes "Related work").  The
 // kernel derives lambda = exp(lq1.lk1) - exp(lq2.lk2) + lambda_init from the
-// four 64-wide parameter vectors (one lane per component, a wave-wide sum),
+// four Dh-wide parameter vectors (one lane per component, a wave-wide sum),
 // keeps A = O1/l1 - lambda O2/l2 in fp32, and stores
 // (1 - lambda_init) * gamma * A / sqrt(mean(A^2) + eps) per row: each query
 // row's Dv values sit in one lane pair, so the row's sum of squares is an
@@ -35,11 +36,11 @@ namespace {
 constexpr int BM = kAttnBM;
 constexpr int BN = 32;   // keys per KV tile (register budget: two score tiles, two accumulators)
 constexpr int NT = 256;
-constexpr int DH = 64;   // width of one Q/K half
-constexpr int DQ = 2 * DH;
 
-template <int DV, bool HEAD>
+// DH: width of one Q/K half (32 or 64); DV: width of V and of the output
+template <int DH, int DV, bool HEAD>
 __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) {
+  constexpr int DQ = 2 * DH;
   constexpr int NDS = DH / 16;          // QK^T k-steps per branch
   constexpr int NDB = DV / 32;          // O^T d-blocks per branch
   constexpr int NPS = BN / 16;          // PV k-steps
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
   // A = O1 / l1 - lambda * O2 / l2 (fp32, in place in o1)
   float lam = a.lambda;
   if constexpr (HEAD) {
-    const float d1 = wave_sum(a.lam_q1[lane] * a.lam_k1[lane]);
-    const float d2 = wave_sum(a.lam_q2[lane] * a.lam_k2[lane]);
+    const float d1 = wave_sum(lane < DH ? a.lam_q1[lane] * a.lam_k1[lane] : 0.f);
+    const float d2 = wave_sum(lane < DH ? a.lam_q2[lane] * a.lam_k2[lane] : 0.f);
     lam = expf(d1) - expf(d2) + a.lambda_init;
   }
   const float l1 = xhalf_sum(st1.l), l2 = xhalf_sum(st2.l);
@@ -207,21 +208,30 @@ __global__ __launch_bounds__(NT, 2) void diff_attn_fwd_kernel(const DiffArgs a) 
   }
 }
 
-}  // namespace
-
-hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dv, hipStream_t stream) {
+template <int DH>
+hipError_t launch_diff_dh(const DiffArgs& a, int Dv, hipStream_t stream) {
   const bool head = a.lam_q1 != nullptr;
   if (Dv == 64 && !head)
-    hipLaunchKernelGGL((diff_attn_fwd_kernel<64, false>), dim3(a.total), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<DH, 64, false>), dim3(a.total), dim3(NT), 0, stream, a);
   else if (Dv == 64)
-    hipLaunchKernelGGL((diff_attn_fwd_kernel<64, true>), dim3(a.total), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<DH, 64, true>), dim3(a.total), dim3(NT), 0, stream, a);
   else if (Dv == 128 && !head)
-    hipLaunchKernelGGL((diff_attn_fwd_kernel<128, false>), dim3(a.total), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<DH, 128, false>), dim3(a.total), dim3(NT), 0, stream, a);
   else if (Dv == 128)
-    hipLaunchKernelGGL((diff_attn_fwd_kernel<128, true>), dim3(a.total), dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((diff_attn_fwd_kernel<DH, 128, true>), dim3(a.total), dim3(NT), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_diff_attn_fwd(const DiffArgs& a, int Dh, int Dv, hipStream_t stream) {
+  switch (Dh) {
+    case 32: return launch_diff_dh<32>(a, Dv, stream);
+    case 64: return launch_diff_dh<64>(a, Dv, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace av

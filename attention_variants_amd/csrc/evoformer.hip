@@ -18,7 +18,7 @@
 //     in fp32 before its one bf16 rounding, so the attention kernel's raw
 //     scores are already scaled and the pair bias becomes the initial
 //     accumulator of the QK^T MFMA.
-//  2. the fused attention kernel at D = dh = 32 with the pair bias as score
+//  2. the fused attention kernel at D = dh (32 or 64) with the pair bias as score
 //     modifier and the sigmoid gate + token-major store as epilogue; each
 //     (sequence, head, 128-residue tile) is one workgroup, sequences vary
 //     fastest within a head so bias[h] stays resident in L2.
@@ -49,7 +49,9 @@ __device__ __forceinline__ int w_off(int row, int c) { return row * GN + (c ^ (w
 // channels x (GM / WM) tokens.  The 256 x 256 form (8 waves) reads half the
 // operand bytes per FLOP of the 128 x 128 form (with K = Cm = 256 the MFMAs
 // are a small part of the time) but holds one workgroup per CU.
-template <int GM, int GN, int NT>
+// DH: head width (32 or 64), which sets how the C tile splits into the
+// head-major planes.
+template <int GM, int GN, int NT, int DH>
 __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const EvoArgs a) {
   constexpr int NW = NT / 64;
   constexpr int WN = GN / 64;            // waves along the channels
@@ -171,8 +173,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const E
   // Epilogue through LDS: the GM x GN bf16 C tile is staged token-major (row
   // pitch CP keeps rows 16-byte aligned; the 32 tokens of one 8-byte write
   // spread over the banks with at most 2-way conflicts), then written out as
-  // 16-byte chunks.  In the head-major planes the 32 channels of one head are
-  // 64 contiguous bytes per token, so consecutive tokens of one head form one
+  // 16-byte chunks.  In the head-major planes the DH channels of one head are
+  // 2*DH contiguous bytes per token, so consecutive tokens of one head form one
   // contiguous run.
   __syncthreads();  // every wave is done with the staging tiles
   bf16* Cs = lds;
@@ -194,21 +196,21 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void evo_proj_kernel(const E
   __syncthreads();
   const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
   bf16* out = (bf16*)a.ws + (size_t)p * plane;
-  constexpr int CPT = 4;                 // 16-byte chunks per token and head (dh = 32: 64 bytes)
-  constexpr int HPT = GN / 32;           // heads per channel tile
+  constexpr int CPT = DH / 8;            // 16-byte chunks per token and head
+  constexpr int HPT = GN / DH;           // heads per channel tile
   constexpr int NCHUNK = GM * HPT * CPT / NT;
   static_assert(GM * HPT * CPT % NT == 0, "chunk/thread mismatch");
-  const int h0 = c0 / 32;
+  const int h0 = c0 / DH;
 #pragma unroll
   for (int k = 0; k < NCHUNK; ++k) {
     const int id = tid + NT * k;
     const int hl = id / (GM * CPT);
     const int rem = id % (GM * CPT);
-    const int tl = rem >> 2, e8 = rem & 3;
+    const int tl = rem / CPT, e8 = rem % CPT;
     const int tok = mt * GM + tl;
     if (tok >= M) continue;
     const int outer = tok / Linner, inner = tok % Linner;
-    const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * 32 + e8 * 8];
+    const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * DH + e8 * 8];
     *(i32x4*)(out + (((size_t)outer * a.H + h0 + hl) * Linner + inner) * a.dh + e8 * 8) = v;
   }
 }
@@ -235,6 +237,7 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr int PP_K = 256;            // Cm of this form
 constexpr int PP_MP = PP_K + 8;      // m tile pitch: 16 consecutive rows -> 16 distinct 16-byte bank groups
 constexpr int PP_BLOCKS = 256;       // 8 XCDs x 32 CUs
+template <int DH>
 __global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoArgs a) {
   constexpr int NT = 512, GM = 128, GN = 128, WN = GN / 64, MB = 1;
   constexpr int MCH = GM * PP_K / 8 / NT;  // 16-byte m chunks per thread per token tile
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoAr
   const float os = p == 0 ? a.scale : 1.f;  // q plane: softmax scale folded in
   const size_t plane = (size_t)a.Ns * a.H * a.Nr * a.dh;
   const auto ors = make_rsrc((bf16*)a.ws + (size_t)p * plane, (uint32_t)(plane * 2));
-  const int h0 = c0 / 32;
+  const int h0 = c0 / DH;
 
   if (stream < Mt) mload(stream);
   lds_barrier();  // W is stored
@@ -339,8 +342,8 @@ __global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoAr
       }
     }
     lds_barrier();
-    constexpr int CPT = 4;        // 16-byte chunks per token and head (dh = 32: 64 bytes)
-    constexpr int HPT = GN / 32;  // heads per channel tile
+    constexpr int CPT = DH / 8;   // 16-byte chunks per token and head
+    constexpr int HPT = GN / DH;  // heads per channel tile
     constexpr int NCHUNK = GM * HPT * CPT / NT;
     static_assert(GM * HPT * CPT % NT == 0, "chunk/thread mismatch");
 #pragma unroll
@@ -348,17 +351,36 @@ __global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoAr
       const int id = tid + NT * k;
       const int hl = id / (GM * CPT);
       const int rem = id % (GM * CPT);
-      const int tl = rem >> 2, e8 = rem & 3;
+      const int tl = rem / CPT, e8 = rem % CPT;
       // tokens past M land past the plane and the buffer store drops them:
       // every tile issues the same four stores, so the next tile's wait for
       // its prefetched m rows can leave these stores in flight
       const int tok = mt * GM + tl;
       const int outer = tok / Linner, inner = tok % Linner;
-      const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * 32 + e8 * 8];
+      const i32x4 v = *(const i32x4*)&Cs[tl * CP + hl * DH + e8 * 8];
       __builtin_amdgcn_raw_buffer_store_b128(
           v, ors, (uint32_t)((((outer * a.H + h0 + hl) * Linner + inner) * a.dh + e8 * 8) * 2), 0, 0);
     }
   }
+}
+
+template <int DH>
+hipError_t launch_evo_proj(const EvoArgs& a, hipStream_t stream) {
+  const int M = a.Ns * a.Nr, HD = a.H * a.dh, N = 4 * HD;
+  // The 256 x 256 tile (one workgroup per CU) pays once its grid fills the
+  // 256 CUs at least four times over (N_res = 768 at 128 sequences: -5 %);
+  // smaller grids keep the 128 x 128 tile at two workgroups per CU.
+  const long long big_tiles = (long long)((M + 255) / 256) * (N / 256);
+  if (a.Cm == PP_K && N % 128 == 0 && 32 % (N / 128) == 0) {
+    hipLaunchKernelGGL((evo_proj_persistent_kernel<DH>), dim3(PP_BLOCKS), dim3(512), 0, stream, a);
+  } else if (HD % 256 == 0 && big_tiles >= 4 * 256) {
+    hipLaunchKernelGGL((evo_proj_kernel<256, 256, 512, DH>), dim3(((M + 255) / 256) * (N / 256)), dim3(512), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((evo_proj_kernel<128, 128, 256, DH>), dim3(((M + 127) / 128) * (N / 128)), dim3(256), 0,
+                       stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -366,19 +388,7 @@ __global__ __launch_bounds__(512, 1) void evo_proj_persistent_kernel(const EvoAr
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
 
 hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
-  const int M = a.Ns * a.Nr, HD = a.H * a.dh, N = 4 * HD;
-  // The 256 x 256 tile (one workgroup per CU) pays once its grid fills the
-  // 256 CUs at least four times over (N_res = 768 at 128 sequences: -5 %);
-  // smaller grids keep the 128 x 128 tile at two workgroups per CU.
-  const long long big_tiles = (long long)((M + 255) / 256) * (N / 256);
-  if (a.Cm == PP_K && N % 128 == 0 && 32 % (N / 128) == 0) {
-    hipLaunchKernelGGL(evo_proj_persistent_kernel, dim3(PP_BLOCKS), dim3(512), 0, stream, a);
-  } else if (HD % 256 == 0 && big_tiles >= 4 * 256) {
-    hipLaunchKernelGGL((evo_proj_kernel<256, 256, 512>), dim3(((M + 255) / 256) * (N / 256)), dim3(512), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((evo_proj_kernel<128, 128, 256>), dim3(((M + 127) / 128) * (N / 128)), dim3(256), 0, stream, a);
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = a.dh == 64 ? launch_evo_proj<64>(a, stream) : launch_evo_proj<32>(a, stream);
   if (e != hipSuccess) return e;
 
   // attention problems: row-wise, one per (sequence, head) over the residues;
@@ -402,13 +412,13 @@ hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
   t.Hq = t.Hkv = a.H;
   t.Sq = t.Skv = L;
   t.g = 1;
-  const int bm = attn_bm(32, a.col ? SM_GATE : SM_BIAS, MK_NONE);
+  const int bm = attn_bm(a.dh, a.col ? SM_GATE : SM_BIAS, MK_NONE);
   t.nM = (L + bm - 1) / bm;
   t.total = nB * a.H * t.nM;
   t.c = kLog2e;  // q arrives scaled
   t.scale = 1.f;
   t.softcap = 1.f;
-  return launch_evo_attention(t, a.col, stream);
+  return launch_evo_attention(t, a.dh, a.col, stream);
 }
 
 }  // namespace av

@@ -349,29 +349,31 @@ def run_sweep(path, steps, warmup):
                   "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                   "hbm_gbs_incl_bias_once": round(by / (per[0] * 1e-3) / 1e9, 1)})
         del bias
-    for S in (1024, 4096, 16384):
-        B = 16384 // S
-        x = wi.diff_inputs(B, 16, S)
-        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
-        out = torch.empty_like(v)
-        try:
+    # differential attention: 16 heads with halves of 64 and V of 128, and 32
+    # heads with halves of 32 and V of 64 (visible work 2 * 2*Dh + 2*Dv per pair)
+    for (H, Dh, Dv) in ((16, 64, 128), (32, 32, 64)):
+        for S in (1024, 4096, 16384):
+            B = 16384 // S
+            x = wi.diff_inputs(B, H, S, Dh, Dv)
+            q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+            out = torch.empty_like(v)
             _, per = time_launches([lambda: av.diff_attn_fwd(q, k, v, out=out)], steps, warmup)
-        except RuntimeError as e:  # not built in this library version
-            emit({"kernel": "diff_attn_fwd", "S": S, "error": str(e)})
-            continue
-        pairs = B * 16 * S * (S + 1) // 2
-        tf = pairs * 512 / (per[0] * 1e-3) / 1e12
-        emit({"kernel": "diff_attn_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
-              "visible_tflops": round(tf, 1), "executed_tflops": round(tf * 1.5, 1),
-              "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
-        # the full head (lambda re-parameterisation and per-row RMSNorm fused in the epilogue)
-        hp = {n: torch.from_numpy(a).to(dev) for n, a in wi.diff_head_params(64, 128).items()}
-        _, per = time_launches([lambda: av.diff_head_fwd(q, k, v, hp["lq1"], hp["lk1"], hp["lq2"], hp["lk2"],
-                                                         lambda_init=0.2, gamma=hp["gamma"], out=out)],
-                               steps, warmup)
-        tf = pairs * 512 / (per[0] * 1e-3) / 1e12
-        emit({"kernel": "diff_head_fwd", "B": B, "H": 16, "S": S, "us": round(per[0] * 1e3, 2),
-              "visible_tflops": round(tf, 1), "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+            pairs = B * H * S * (S + 1) // 2
+            fpp = 4 * Dh + 2 * Dv
+            tf = pairs * fpp / (per[0] * 1e-3) / 1e12
+            emit({"kernel": "diff_attn_fwd", "B": B, "H": H, "S": S, "Dh": Dh, "Dv": Dv,
+                  "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
+                  "executed_tflops": round(tf * (fpp + 2 * Dv) / fpp, 1),
+                  "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
+            # the full head (lambda re-parameterisation and per-row RMSNorm fused in the epilogue)
+            hp = {n: torch.from_numpy(a).to(dev) for n, a in wi.diff_head_params(Dh, Dv).items()}
+            _, per = time_launches([lambda: av.diff_head_fwd(q, k, v, hp["lq1"], hp["lk1"], hp["lq2"], hp["lk2"],
+                                                             lambda_init=0.2, gamma=hp["gamma"], out=out)],
+                                   steps, warmup)
+            tf = pairs * fpp / (per[0] * 1e-3) / 1e12
+            emit({"kernel": "diff_head_fwd", "B": B, "H": H, "S": S, "Dh": Dh, "Dv": Dv,
+                  "us": round(per[0] * 1e3, 2), "visible_tflops": round(tf, 1),
+                  "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
     # backward at the headline shape (algorithmic work: 5 products of 2*S*S*D
     # per head, i.e. 2.5x the forward's visible FLOPs)
     for (sm, mk) in (("none", "none"), ("softcap", "causal")):
@@ -423,8 +425,9 @@ def run_sweep(path, steps, warmup):
         emit({"kernel": "attn_decode_paged_fwd", "score_mod": "softcap", "mask": "causal", "B": B, "Hq": Hq,
               "Hkv": Hkv, "Sq": 1, "Skv": Skv, "page_size": ps, "D": D, "us": round(per[0] * 1e3, 2),
               "hbm_gbs": round(byts / (per[0] * 1e-3) / 1e9, 1), "frac_hbm_peak": round(byts / (per[0] * 1e-3) / 8e12, 4)})
-    for Nr in (256, 384, 768):
-        Ns, Cm, Hh, dh = 128, 256, 8, 32
+    # Evoformer: the AlphaFold2 head shape 8 x 32 and the kernel-benchmark 4 x 64
+    for (Hh, dh, Nr) in [(8, 32, n) for n in (256, 384, 768)] + [(4, 64, n) for n in (256, 384, 768)]:
+        Ns, Cm = 128, 256
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
         t = {n: _dev(x[n], dev) for n in x}
         ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
@@ -438,7 +441,8 @@ def run_sweep(path, steps, warmup):
             continue
         fl = 2 * Ns * Nr * Cm * 4 * Hh * dh + 4 * Ns * Hh * Nr * Nr * dh
         tf = fl / (per[0] * 1e-3) / 1e12
-        emit({"kernel": "evoformer_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "us": round(per[0] * 1e3, 2),
+        emit({"kernel": "evoformer_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "H": Hh, "dh": dh,
+              "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         # column-wise form on the same MSA: attention over the 128 sequences of each residue column
         _, per = time_launches([lambda: av.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"],
@@ -446,7 +450,8 @@ def run_sweep(path, steps, warmup):
                                steps, warmup)
         fl = 2 * Ns * Nr * Cm * 4 * Hh * dh + 4 * Nr * Hh * Ns * Ns * dh
         tf = fl / (per[0] * 1e-3) / 1e12
-        emit({"kernel": "evoformer_col_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "us": round(per[0] * 1e3, 2),
+        emit({"kernel": "evoformer_col_gated_attn_fwd", "Ns": Ns, "Nr": Nr, "H": Hh, "dh": dh,
+              "us": round(per[0] * 1e3, 2),
               "visible_tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
     f.close()
 

@@ -233,7 +233,9 @@ int attn_bwd(const av_variant* variant, const void* q, const void* k, const void
  *   v    [B, H, S, Dv],  out [B, H, S, Dv]
  *   out = (softmax(scale * q1 k1^T + M) - lambda * softmax(scale * q2 k2^T + M)) v
  * M is the causal mask when `causal` != 0, else nothing.  scale = 0 selects
- * 1/sqrt(Dh).  Supported: Dh = 64, Dv in {64, 128}. */
+ * 1/sqrt(Dh).  Supported: Dh in {32, 64}, Dv in {64, 128} (the talk notes'
+ * "16 heads x 128" shape read as Dh = 64, Dv = 128; "32 heads x 64" as
+ * Dh = 32, Dv = 64). */
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh,
                   int Dv, float lambda, float scale, int causal, hipStream_t stream);
 
@@ -269,7 +271,9 @@ int diff_head_fwd(const void* q, const void* k, const void* v, const float* lamb
  * at least evoformer_workspace_bytes(...) bytes, 256-byte aligned) by one
  * kernel, then consumed by the attention kernel; the q plane holds scale*q
  * (the softmax scale applied before the bf16 rounding).  scale = 0 selects
- * 1/sqrt(dh).  Supported: dh = 32, Cm a multiple of 64, H*dh a multiple of 128. */
+ * 1/sqrt(dh).  Supported: dh in {32, 64} (the AlphaFold2 8 heads x 32 and the talk
+ * notes' kernel-benchmark 4 heads x 64), Cm a multiple of 64, H*dh a multiple
+ * of 128. */
 size_t evoformer_workspace_bytes(int Ns, int Nr, int H, int dh);
 int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
                              const void* bias, void* out, void* workspace, size_t workspace_bytes, int Ns,

@@ -171,7 +171,7 @@ def test_diff_attn_rejections(lib):
     assert call(o=None) == -1
     assert call(B=0) == -2
     assert call(S=-3) == -2
-    assert call(Dh=32) == -3
+    assert call(Dh=16) == -3
     assert call(Dv=96) == -3
     assert call(lam=float("nan")) == -7
     assert call(scale=-2.0) == -7
@@ -191,7 +191,7 @@ def test_diff_head_rejections(lib):
     assert call(lq1=None) == -1
     assert call(lk2=None) == -1
     assert call(B=0) == -2
-    assert call(Dh=32) == -3
+    assert call(Dh=48) == -3
     assert call(Dv=96) == -3
     assert call(lam_init=float("inf")) == -7
     assert call(eps=0.0) == -7
@@ -218,7 +218,7 @@ def test_evoformer_rejections(lib):
     assert call(w=None) == -1
     assert call(bias=None) == -1
     assert call(Ns=0) == -2
-    assert call(dh=64) == -3
+    assert call(dh=48) == -3
     assert call(Cm=48) == -3
     assert call(H=2) == -3  # H*dh must be a multiple of 128
     assert call(scale=float("nan")) == -7

@@ -21,16 +21,17 @@ from .gpu_util import assert_close, canary_empty, canary_intact, f64, sample_row
 pytestmark = pytest.mark.gpu
 
 
-def _params(Dv, seed=17, scale_lam=1.0):
-    p = wi.diff_head_params(64, Dv, seed)
+def _params(Dv, seed=17, scale_lam=1.0, Dh=64):
+    p = wi.diff_head_params(Dh, Dv, seed)
     for n in ("lq1", "lk1", "lq2", "lk2"):
         p[n] = (p[n] * np.float32(scale_lam)).astype(np.float32)
     return p
 
 
-def _run(av, B, H, S, Dv=128, causal=True, rows=None, p=None, lambda_init=None, use_gamma=True, eps=1e-5):
-    x = wi.diff_inputs(B, H, S, 64, Dv)
-    p = _params(Dv) if p is None else p
+def _run(av, B, H, S, Dv=128, causal=True, rows=None, p=None, lambda_init=None, use_gamma=True, eps=1e-5,
+         Dh=64):
+    x = wi.diff_inputs(B, H, S, Dh, Dv)
+    p = _params(Dv, Dh=Dh) if p is None else p
     lambda_init = oracle.diff_lambda_init(3) if lambda_init is None else lambda_init
     q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
     dp = {n: torch.from_numpy(p[n]).cuda() for n in p}
@@ -46,7 +47,7 @@ def _run(av, B, H, S, Dv=128, causal=True, rows=None, p=None, lambda_init=None, 
     got = out.float().cpu().numpy()
     if rows is not None:
         got = got[:, :, rows]
-    return assert_close(got, ref, f"diff head B{B} H{H} S{S} Dv{Dv} causal{causal} gamma{use_gamma}"), out
+    return assert_close(got, ref, f"diff head B{B} H{H} S{S} Dh{Dh} Dv{Dv} causal{causal} gamma{use_gamma}"), out
 
 
 @pytest.mark.parametrize("S", [1, 17, 32, 129, 300])
@@ -54,6 +55,7 @@ def _run(av, B, H, S, Dv=128, causal=True, rows=None, p=None, lambda_init=None, 
 def test_small_all_rows(gpu_lib, S, causal):
     _run(gpu_lib, 2, 3, S, causal=causal)
     _run(gpu_lib, 1, 2, S, Dv=64, causal=causal, use_gamma=False)
+    _run(gpu_lib, 2, 3, S, Dh=32, Dv=64, causal=causal)
 
 
 @pytest.mark.parametrize("scale_lam,lambda_init", [(0.0, 0.2), (3.0, 0.8), (6.0, 0.35), (1.0, -0.5)])

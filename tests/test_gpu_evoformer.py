@@ -86,6 +86,22 @@ def test_benchmark_shapes(gpu_lib, Nr):
     _run(gpu_lib, 128, Nr, seqs=seqs, rows=rows)
 
 
+@pytest.mark.parametrize("Nr", [1, 17, 100, 129])
+def test_head_width_64_all_rows(gpu_lib, Nr):
+    """4 heads x 64 (the talk notes' Evoformer kernel-benchmark head shape), every row."""
+    _run(gpu_lib, 3, Nr, Cm=128, H=4, dh=64)
+    _run(gpu_lib, 2, Nr, Cm=256, H=4, dh=64)
+
+
+@pytest.mark.parametrize("Nr", [256, 384, 768])
+def test_benchmark_shapes_4x64(gpu_lib, Nr):
+    """128 sequences, 4 heads x 64, Cm 256: sampled sequences and residues as above."""
+    rng = np.random.default_rng(8)
+    seqs = np.unique(np.concatenate([np.arange(0, 128, 8), [1, 127], rng.integers(0, 128, 4)]))
+    rows = np.unique(np.concatenate([[0, 1, Nr - 1, 127, 128, Nr // 2], rng.integers(0, Nr, 40)]))
+    _run(gpu_lib, 128, Nr, H=4, dh=64, seqs=seqs, rows=rows)
+
+
 def test_pair_bias_minus_inf(gpu_lib):
     """A pair bias of -inf drops the pair (the bias enters the QK^T MFMA as its
     initial accumulator, where -inf stays -inf); about a third of the pairs

@@ -87,3 +87,18 @@ def test_benchmark_shapes(gpu_lib, Nr):
     seqs = np.unique(np.concatenate([[0, 1, 63, 64, 127], rng.integers(0, 128, 12)]))
     cols = np.unique(np.concatenate([[0, 1, Nr - 1, Nr // 2], rng.integers(0, Nr, 12)]))
     _run(gpu_lib, 128, Nr, seqs=seqs, cols=cols)
+
+
+@pytest.mark.parametrize("Ns", [1, 33, 128, 130])
+def test_head_width_64(gpu_lib, Ns):
+    """4 heads x 64, every column of a small MSA."""
+    _run(gpu_lib, Ns, 7, Cm=128, H=4, dh=64)
+    _run(gpu_lib, Ns, 5, Cm=256, H=4, dh=64)
+
+
+@pytest.mark.parametrize("Nr", [256, 768])
+def test_benchmark_shapes_4x64(gpu_lib, Nr):
+    rng = np.random.default_rng(9)
+    seqs = np.unique(np.concatenate([[0, 1, 63, 64, 127], rng.integers(0, 128, 12)]))
+    cols = np.unique(np.concatenate([[0, 1, Nr - 1, Nr // 2], rng.integers(0, Nr, 28)]))
+    _run(gpu_lib, 128, Nr, H=4, dh=64, seqs=seqs, cols=cols)
