@@ -425,9 +425,11 @@ def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) -> int:
 
 
 def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
-             alibi_max_bias=8.0, kv_group=0, dq=None, dk=None, dv=None, workspace=None):
+             alibi_max_bias=8.0, window=256, prefix_len=0, doc_id=None, kv_group=0, dq=None, dk=None, dv=None,
+             workspace=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for an upstream ``dout``; ``lse``
-    is attn_fwd's (``return_lse=True``).  Masks: none or causal."""
+    is attn_fwd's (``return_lse=True``).  Every mask of attn_fwd, with the same
+    ``window`` / ``prefix_len`` / ``doc_id``."""
     import torch
 
     lib = load_library()
@@ -454,12 +456,14 @@ def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, so
         dv = torch.empty_like(v)
     else:
         _need_shape(dv, "dv", torch.bfloat16, (B, Hkv, Skv, D), dev)
+    if doc_id is not None:
+        _need_shape(doc_id, "doc_id", torch.int32, (B, Sq), dev)
     need = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
-                       kv_group=kv_group)
+                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group)
     rc = lib.attn_bwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                       ws_bytes, B, Hq, Hkv, Sq, Skv, D, _stream_ptr(dev))

@@ -9,6 +9,10 @@
 //   dV = P^T dO,   dP = dO V^T,   dT = P (dP - Delta),  Delta = rowsum(P dP)
 //   dS = dT mod'(scale q.k)   (softcap: 1 - tanh^2; none / ALiBi: 1)
 //   dQ = scale dS K,   dK = scale dS^T Q
+// Masks: the forward's five (none, causal, sliding window, PrefixLM,
+// document), with the forward's analytic tile ranges on both sides: the
+// query-owner launches walk only the key tiles a query tile can see, the
+// key-owner launch only the query tiles that can see its keys.
 // Three launches over the same forward-shaped and key-owner layouts:
 //  1. row statistics: per query row, with the forward's lse only as an
 //     exponent reference, l = sum exp(t - lse) and Delta = sum exp(t - lse) dP / l,
@@ -51,6 +55,17 @@ __device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, f
   }
 }
 
+// Whether key kp is visible to query q under mask MK (the forward's
+// predicates); qd and kd are the two rows' document ids (document mask).
+template <int MK>
+__device__ __forceinline__ bool bwd_visible(const BwdArgs& a, int q, int kp, int qd, int kd) {
+  if constexpr (MK == MK_CAUSAL) return kp <= q;
+  if constexpr (MK == MK_WINDOW) return kp <= q && q - kp < a.window;
+  if constexpr (MK == MK_PREFIX) return kp < a.prefix || kp <= q;
+  if constexpr (MK == MK_DOC) return qd == kd;
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 128 keys of one (b, KV head); wave w owns keys
 // k0 + 32 w .. +31, held in registers as the B operand of S = Q K^T and
@@ -58,20 +73,22 @@ __device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, f
 // every query head of the group are staged in LDS, row-major and swizzled,
 // and read two ways: rows for the A operand of S and dP, transposed for the
 // A operand of dV^T += dO^T P and dK^T += Q^T dS.
-template <int SM, bool CAUSAL>
+template <int SM, int MK>
 __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
   constexpr int BQ = 64;
   constexpr int QCH = BQ * CPR / NT;  // 16-byte chunks per thread per tensor
+  constexpr bool kDoc = MK == MK_DOC;
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
   __shared__ __attribute__((aligned(16))) bf16 Gs[2][BQ * D];  // dO
   __shared__ __attribute__((aligned(16))) float Ls[2][BQ];     // lse in log2 units (+inf past Sq)
   __shared__ __attribute__((aligned(16))) float Es[2][BQ];     // Delta
+  __shared__ __attribute__((aligned(16))) int Dq[2][kDoc ? BQ : 1];  // document ids of the query rows
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int nKT = (a.Skv + 127) / 128;
   int kt, bk;
-  if constexpr (CAUSAL) {  // key tile 0 is reached by every query: heaviest first
+  if constexpr (MK == MK_CAUSAL || MK == MK_PREFIX) {  // key tile 0 is reached by every query: heaviest first
     const TileIdx ti = weighted_tile(blockIdx.x, a.total, nKT);
     kt = ti.mt_lin;
     bk = ti.bh;
@@ -99,16 +116,39 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dkT[db] = dvT[db] = f32x16{};
   const TrLane<D> tl(lane);
   const bool key_live = key < a.Skv;
+  const int* docrow = kDoc ? a.doc + (size_t)b * a.Skv : nullptr;
+  const int kdoc = kDoc ? docrow[min(key, a.Skv - 1)] : 0;
+  const int kwlast = min(kw0 + 31, a.Skv - 1);  // last key of this wave
+  int kd_lo = 0, kd_hi = 0;                     // document ids of the wave's first and last key
+  if constexpr (kDoc) {
+    kd_lo = __builtin_amdgcn_readfirstlane(docrow[min(kw0, a.Skv - 1)]);
+    kd_hi = __builtin_amdgcn_readfirstlane(docrow[kwlast]);
+  }
 
-  // work items: (query head of the group, 64-row query tile); causal: only
-  // tiles that reach this workgroup's keys
+  // work items: (query head of the group, 64-row query tile), over the query
+  // tiles that can see this workgroup's keys [k0, klast]
   const int nQT = (a.Sq + BQ - 1) / BQ;
-  const int qt_lo = CAUSAL ? k0 / BQ : 0;
-  const int per_head = max(nQT - qt_lo, 0);
+  const int klast = min(k0 + 127, a.Skv - 1);
+  int qt_lo = 0, qt_hi = nQT;
+  if constexpr (MK == MK_CAUSAL) {
+    qt_lo = k0 / BQ;
+  } else if constexpr (MK == MK_WINDOW) {
+    qt_lo = k0 / BQ;
+    qt_hi = min(nQT, (klast + a.window - 1) / BQ + 1);
+  } else if constexpr (MK == MK_PREFIX) {
+    qt_lo = k0 < a.prefix ? 0 : k0 / BQ;
+  } else if constexpr (MK == MK_DOC) {
+    const int qstart = wave_lower_bound(docrow, a.Sq, docrow[k0]);
+    const int qend = wave_upper_bound(docrow, a.Sq, docrow[klast]);
+    qt_lo = qstart / BQ;
+    qt_hi = min(nQT, (qend + BQ - 1) / BQ);
+  }
+  const int per_head = max(qt_hi - qt_lo, 0);
   const int n_items = a.g * per_head;
 
   i32x4 qr[QCH], gr[QCH];
   float lr = 0.f, er = 0.f;
+  int dr = 0;
   auto gload = [&](int item) {
     const int hq = hk * a.g + item / per_head;
     const int qt = qt_lo + item % per_head;
@@ -127,6 +167,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
       const size_t r = ((size_t)b * a.Hq + hq) * a.Sq + q;
       lr = q < a.Sq ? a.stats[2 * r] : __builtin_inff();
       er = q < a.Sq ? a.stats[2 * r + 1] : 0.f;
+      if constexpr (kDoc) dr = q < a.Sq ? docrow[q] : -1;
     }
   };
   auto sstore = [&](int buf) {
@@ -139,6 +180,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
     if (tid < BQ) {
       Ls[buf][tid] = lr;
       Es[buf][tid] = er;
+      if constexpr (kDoc) Dq[buf][tid] = dr;
     }
   };
 
@@ -155,8 +197,20 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int qb0 = qt * BQ + 32 * blk;  // first query of the block
-      if (CAUSAL && kw0 > qb0 + 31) continue;  // every key of the wave after every query
-      if (!__builtin_amdgcn_readfirstlane((int)(kw0 < a.Skv))) continue;
+      const int qblast = qb0 + 31;
+      // skip the block when no key of the wave is visible to any of its queries
+      bool skip = kw0 >= a.Skv || qb0 >= a.Sq;
+      if constexpr (MK == MK_CAUSAL) {
+        skip |= kw0 > qblast;
+      } else if constexpr (MK == MK_WINDOW) {
+        skip |= kw0 > qblast || qb0 - kwlast >= a.window;
+      } else if constexpr (MK == MK_PREFIX) {
+        skip |= kw0 >= a.prefix && kw0 > qblast;
+      } else if constexpr (MK == MK_DOC) {
+        const int qd_lo = Dq[buf][32 * blk], qd_hi = Dq[buf][32 * blk + 31];
+        skip |= kd_hi < qd_lo || (kd_lo > qd_hi && qd_hi >= 0);
+      }
+      if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
       // S = Q K^T, dP = dO V^T: lane = key, registers = queries qb0 + 8(j/4) + 4hh + j%4
       f32x16 sc = {}, dp = {};
 #pragma unroll
@@ -177,8 +231,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
           const float bias = SM == SM_ALIBI ? slope2 * (float)(key - q) : 0.f;
           float dmod;
           float p = bwd_prob<SM>(a, sc[j], l4[e], bias, dmod);
-          bool ok = key_live;
-          if constexpr (CAUSAL) ok = ok && (key <= q);
+          const int qd = kDoc ? Dq[buf][32 * blk + 8 * g4 + 4 * hh + e] : 0;
+          const bool ok = key_live && bwd_visible<MK>(a, q, key, qd, kdoc);
           p = ok ? p : 0.f;
           const float ds = p * (dp[j] - e4[e]) * dmod;
           const bf16 ph = (bf16)p;
@@ -233,18 +287,21 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 // dQ^T += K^T dS^T with K^T read transposed.
 // STATS = true is launch 1 (row statistics): the same loop without the dQ
 // product, summing p and p * dP per row.
-template <int SM, bool CAUSAL, bool STATS>
+template <int SM, int MK, bool STATS>
 __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BN = 64;
   constexpr int NCH = BN * CPR / NT;
+  constexpr bool kDoc = MK == MK_DOC;
+  constexpr bool kWeighted = MK == MK_CAUSAL || MK == MK_PREFIX;  // later query tiles see more keys
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * D];
+  __shared__ __attribute__((aligned(16))) int Dk[2][kDoc ? BN : 1];  // document ids of the keys
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
   const int nM = (a.Sq + 127) / 128;
   int mt_lin, bh;
-  if constexpr (CAUSAL) {
+  if constexpr (kWeighted) {
     const TileIdx ti = weighted_tile(blockIdx.x, a.total_q, nM);
     mt_lin = ti.mt_lin;
     bh = ti.bh;
@@ -255,7 +312,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   }
   const int hq = bh % a.Hq, b = bh / a.Hq;
   const int hk = hq / a.g;
-  const int mt = CAUSAL ? nM - 1 - mt_lin : mt_lin;  // heaviest query tiles first
+  const int mt = kWeighted ? nM - 1 - mt_lin : mt_lin;  // heaviest query tiles first
   const int q0 = mt * 128;
   const int qw = q0 + 32 * __builtin_amdgcn_readfirstlane(w);
   const int q = qw + l32;
@@ -292,11 +349,32 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
   const TrLane<D> tl(lane);
 
+  // the forward's analytic key range of the query tile [q0, qlast]
   const int nKV = (a.Skv + BN - 1) / BN;
-  const int n_hi = CAUSAL ? min(nKV, (min(q0 + 127, a.Sq - 1)) / BN + 1) : nKV;
+  const int qlast = min(q0 + 127, a.Sq - 1);
   const int qwlast = min(qw + 31, a.Sq - 1);
+  const int* docrow = kDoc ? a.doc + (size_t)b * a.Sq : nullptr;
+  int n_lo = 0, n_hi = nKV;
+  int qdoc = 0, qd_lo = 0, qd_hi = 0;
+  if constexpr (MK == MK_CAUSAL) {
+    n_hi = min(nKV, qlast / BN + 1);
+  } else if constexpr (MK == MK_WINDOW) {
+    n_lo = max(0, q0 - a.window + 1) / BN;
+    n_hi = min(nKV, qlast / BN + 1);
+  } else if constexpr (MK == MK_PREFIX) {
+    n_hi = min(nKV, max(a.prefix - 1, qlast) / BN + 1);
+  } else if constexpr (MK == MK_DOC) {
+    const int kstart = wave_lower_bound(docrow, a.Skv, docrow[q0]);
+    const int kend = wave_upper_bound(docrow, a.Skv, docrow[qlast]);
+    n_lo = kstart / BN;
+    n_hi = min(nKV, (kend + BN - 1) / BN);
+    qdoc = docrow[min(q, a.Sq - 1)];
+    qd_lo = __builtin_amdgcn_readfirstlane(docrow[min(qw, a.Sq - 1)]);
+    qd_hi = __builtin_amdgcn_readfirstlane(docrow[max(qwlast, 0)]);
+  }
 
   i32x4 kr[NCH], vr[NCH];
+  int dr = 0;
   auto gload = [&](int nt) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -304,6 +382,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
       const uint32_t off = (uint32_t)((nt * BN + idx / CPR) * D + (idx % CPR) * 8) * 2;
       kr[c] = buf_load16(krs, off);
       vr[c] = buf_load16(vrs, off);
+    }
+    if constexpr (kDoc) {
+      if (tid < BN) {
+        const int kp = nt * BN + tid;
+        dr = kp < a.Skv ? docrow[kp] : 0x7fffffff;
+      }
     }
   };
   auto sstore = [&](int buf) {
@@ -314,17 +398,30 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
       *(i32x4*)&Ks[buf][off] = kr[c];
       *(i32x4*)&Vs[buf][off] = vr[c];
     }
+    if constexpr (kDoc) {
+      if (tid < BN) Dk[buf][tid] = dr;
+    }
   };
 
-  if (n_hi > 0) gload(0);
-  for (int nt = 0; nt < n_hi; ++nt) {
-    const int buf = nt & 1;
+  if (n_lo < n_hi) gload(n_lo);
+  for (int nt = n_lo; nt < n_hi; ++nt) {
+    const int buf = (nt - n_lo) & 1;
     sstore(buf);
     __syncthreads();
     if (nt + 1 < n_hi) gload(nt + 1);
-    const int n0 = nt * BN;
-    if (qw >= a.Sq) continue;
-    if (CAUSAL && n0 > qwlast) continue;
+    const int n0 = nt * BN, n1 = n0 + BN - 1;
+    // skip the tile when none of its keys is visible to this wave's queries
+    bool skip = qw >= a.Sq;
+    if constexpr (MK == MK_CAUSAL) {
+      skip |= n0 > qwlast;
+    } else if constexpr (MK == MK_WINDOW) {
+      skip |= n0 > qwlast || qw - n1 >= a.window;
+    } else if constexpr (MK == MK_PREFIX) {
+      skip |= n0 >= a.prefix && n0 > qwlast;
+    } else if constexpr (MK == MK_DOC) {
+      skip |= Dk[buf][BN - 1] < qd_lo || Dk[buf][0] > qd_hi;
+    }
+    if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
     // S^T, dP^T: lane = query, registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -346,8 +443,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
         const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
         float dmod;
         float p = bwd_prob<SM>(a, sc[kb][j], l2, bias, dmod);
-        bool ok = kp < a.Skv;
-        if constexpr (CAUSAL) ok = ok && (kp <= q);
+        const int kd = kDoc ? Dk[buf][kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)] : 0;
+        const bool ok = kp < a.Skv && bwd_visible<MK>(a, q, kp, qdoc, kd);
         p = ok ? p : 0.f;
         if constexpr (STATS) {
           psum += p;
@@ -399,21 +496,28 @@ __global__ __launch_bounds__(NT) void zero_fill_kernel(i32x4* p, size_t n16) {
   if (i < n16) p[i] = i32x4{0, 0, 0, 0};
 }
 
-template <int SM, bool CAUSAL>
+template <int SM, int MK>
 hipError_t launch_bwd2(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, CAUSAL, true>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, MK, true>), dim3(a.total_q), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<SM, CAUSAL>), dim3(a.total), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<SM, MK>), dim3(a.total), dim3(NT), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, CAUSAL, false>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, MK, false>), dim3(a.total_q), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int SM>
-hipError_t launch_bwd1(const BwdArgs& a, int causal, hipStream_t stream) {
-  return causal ? launch_bwd2<SM, true>(a, stream) : launch_bwd2<SM, false>(a, stream);
+hipError_t launch_bwd1(const BwdArgs& a, int mask, hipStream_t stream) {
+  switch (mask) {
+    case MK_NONE: return launch_bwd2<SM, MK_NONE>(a, stream);
+    case MK_CAUSAL: return launch_bwd2<SM, MK_CAUSAL>(a, stream);
+    case MK_WINDOW: return launch_bwd2<SM, MK_WINDOW>(a, stream);
+    case MK_PREFIX: return launch_bwd2<SM, MK_PREFIX>(a, stream);
+    case MK_DOC: return launch_bwd2<SM, MK_DOC>(a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -425,11 +529,11 @@ hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int causal, hipStream_t stream) {
+hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int mask, hipStream_t stream) {
   switch (score_mod) {
-    case SM_NONE: return launch_bwd1<SM_NONE>(a, causal, stream);
-    case SM_ALIBI: return launch_bwd1<SM_ALIBI>(a, causal, stream);
-    case SM_SOFTCAP: return launch_bwd1<SM_SOFTCAP>(a, causal, stream);
+    case SM_NONE: return launch_bwd1<SM_NONE>(a, mask, stream);
+    case SM_ALIBI: return launch_bwd1<SM_ALIBI>(a, mask, stream);
+    case SM_SOFTCAP: return launch_bwd1<SM_SOFTCAP>(a, mask, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -367,18 +367,22 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
       (Skv > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
     return AV_ERR_NULL;
   if (var->score_mod < AV_SCORE_NONE || var->score_mod > AV_SCORE_SOFTCAP) return AV_ERR_UNSUPPORTED;
-  if (var->mask != AV_MASK_NONE && var->mask != AV_MASK_CAUSAL) return AV_ERR_UNSUPPORTED;
+  if (var->mask < AV_MASK_NONE || var->mask > AV_MASK_DOCUMENT) return AV_ERR_UNSUPPORTED;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq < 0 || Skv < 0 || D <= 0) return AV_ERR_SHAPE;
   if (Hq % Hkv != 0) return AV_ERR_SHAPE;
   if (var->kv_group != 0 && var->kv_group != Hq / Hkv) return AV_ERR_SHAPE;
-  if (var->mask == AV_MASK_CAUSAL && Sq != Skv) return AV_ERR_SHAPE;
+  if (var->mask != AV_MASK_NONE && Sq != Skv) return AV_ERR_SHAPE;
   if (D != 64) return AV_ERR_UNSUPPORTED;
+  if (var->mask == AV_MASK_DOCUMENT && Sq > 0 && var->doc_id == nullptr) return AV_ERR_NULL;
   if (!(isfinite(var->scale) && var->scale >= 0.f)) return AV_ERR_PARAM;
   if (var->score_mod == AV_SCORE_SOFTCAP && !(isfinite(var->softcap) && var->softcap > 0.f)) return AV_ERR_PARAM;
   if (var->score_mod == AV_SCORE_ALIBI && !isfinite(var->alibi_max_bias)) return AV_ERR_PARAM;
+  if (var->mask == AV_MASK_SLIDING_WINDOW && var->window < 1) return AV_ERR_PARAM;
+  if (var->mask == AV_MASK_PREFIX_LM && (var->prefix_len < 0 || var->prefix_len > Sq)) return AV_ERR_PARAM;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return AV_ERR_ALIGN;
+  if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
   if ((uint64_t)(Sq + 128) * D * 2 > kMaxSliceBytes || (uint64_t)(Skv + 128) * D * 2 > kMaxSliceBytes)
     return AV_ERR_TOO_LARGE;
   const int64_t total = (int64_t)B * Hkv * ((Skv + 127) / 128);
@@ -426,7 +430,10 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
   a.sc_k = (float)(2.0 * scale * kLog2e / a.softcap);
   a.alibi_max_bias = var->alibi_max_bias;
-  return hip_status(av::launch_attn_bwd(a, var->score_mod, var->mask == AV_MASK_CAUSAL, stream));
+  a.window = var->window;
+  a.prefix = var->prefix_len;
+  a.doc = var->mask == AV_MASK_DOCUMENT ? var->doc_id : nullptr;
+  return hip_status(av::launch_attn_bwd(a, var->score_mod, var->mask, stream));
 }
 
 int diff_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int S, int Dh, int Dv,

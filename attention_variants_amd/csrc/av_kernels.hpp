@@ -120,7 +120,7 @@ constexpr size_t kDecodeScratchBytes = (size_t)1024 * 32 * (64 + 2) * 4;
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_attn_decode(const DecodeArgs& a, int score_mod, int causal, hipStream_t stream);
 
-// Attention backward (D = 64; masks none / causal).
+// Attention backward (D = 64; the forward's five masks).
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -139,8 +139,11 @@ struct BwdArgs {
   float sc_k;         // softcap: 2 * scale * log2(e) / cap
   float alibi_max_bias;
   float softcap;
+  int window;         // MK_WINDOW
+  int prefix;         // MK_PREFIX
+  const int* doc;     // MK_DOC: [B, S] document ids
 };
-hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int causal, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int mask, hipStream_t stream);
 // Zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel (no memset
 // node, so the call can sit in a captured graph).
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);

@@ -219,8 +219,10 @@ int attn_decode_paged_fwd(const av_variant* variant, const void* q, const void* 
  * and dout [B, Hq, Sq, D].  Outputs dq [B, Hq, Sq, D], dk, dv
  * [B, Hkv, Skv, D], bf16 (fp32 accumulation).  `workspace` (device,
  * caller-owned, 16-byte aligned) holds attn_bwd_workspace_bytes(...) bytes.
- * Supported: D = 64; mask none or causal (causal needs Sq == Skv); every
- * score modifier but AV_SCORE_BIAS.  Deterministic (no atomics). */
+ * Supported: D = 64; every mask of attn_fwd with its parameters in the
+ * variant (window, prefix_len, doc_id; a mask needs Sq == Skv); every score
+ * modifier but AV_SCORE_BIAS.  Sq > 0 with Skv == 0 writes a zero dq.
+ * Deterministic (no atomics). */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
 int attn_bwd(const av_variant* variant, const void* q, const void* k, const void* v, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,

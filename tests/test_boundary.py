@@ -291,8 +291,10 @@ def test_backward_rejections(lib):
 
     assert call(lse=None) == -1
     assert call(dq=None) == -1
-    assert call(mask=2) == -3
-    assert call(Skv=64) == -2          # causal needs Sq == Skv
+    assert call(mask=5) == -3
+    assert call(mask=4) == -1          # the document mask needs doc_id
+    assert call(Skv=64) == -2          # a mask needs Sq == Skv
+    assert call(mask=2, Skv=64) == -2
     assert call(D=128) == -3
     assert call(Hq=3) == -2
     assert call(ws=None) == -5

@@ -19,16 +19,36 @@ from .gpu_util import assert_close, f64, to_dev
 pytestmark = pytest.mark.gpu
 
 
+MASKS = ("none", "causal", "sliding_window", "prefix_lm", "document")
+
+
+def _mask_kw(mask, B, S):
+    """The mask parameters of the forward tests: window 256 from S = 1k (S / 3
+    below), prefix S / 4, seeded document lengths (uniform 64..S/2, 4..S/2
+    below S = 256); returns (oracle kwargs, device kwargs)."""
+    kw = {}
+    if mask == "sliding_window":
+        kw["window"] = 256 if S >= 1024 else max(1, S // 3)
+    if mask == "prefix_lm":
+        kw["prefix_len"] = S // 4
+    dev_kw = dict(kw)
+    if mask == "document":
+        kw["doc_id"] = wi.doc_ids(4, B, S, lo=64 if S >= 256 else 4)
+        dev_kw["doc_id"] = torch.from_numpy(kw["doc_id"]).cuda()
+    return kw, dev_kw
+
+
 def _run(av, B, Hq, Hkv, S, score_mod, mask, seed=(21, 22, 23), dseed=24):
     D = 64
     x = wi.attention_inputs(B, Hq, Hkv, S, S, D, seeds=seed)
     g = wi.normal_bf16(dseed, (B, Hq, S, D), 1.0)
     q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    okw, dkw = _mask_kw(mask, B, S)
     kw = dict(score_mod=score_mod, mask=mask, softcap=20.0)
-    out, lse = av.attn_fwd(q, k, v, return_lse=True, **kw)
-    dq, dk, dv = av.attn_bwd(q, k, v, dout, lse, **kw)
+    out, lse = av.attn_fwd(q, k, v, return_lse=True, **kw, **dkw)
+    dq, dk, dv = av.attn_bwd(q, k, v, dout, lse, **kw, **dkw)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attention_backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g), **kw)
+    rq, rk, rv = oracle.attention_backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g), **kw, **okw)
     what = f"bwd {score_mod}/{mask} B{B} Hq{Hq} Hkv{Hkv} S{S}"
     e = [assert_close(dq.float().cpu().numpy(), rq, what + " dq"),
          assert_close(dk.float().cpu().numpy(), rk, what + " dk"),
@@ -37,7 +57,7 @@ def _run(av, B, Hq, Hkv, S, score_mod, mask, seed=(21, 22, 23), dseed=24):
 
 
 @pytest.mark.parametrize("score_mod", ["none", "alibi", "softcap"])
-@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("mask", MASKS)
 def test_bwd_parity(gpu_lib, score_mod, mask):
     for (B, Hq, Hkv, S) in ((1, 4, 2, 128), (2, 2, 2, 300), (1, 2, 1, 65), (1, 2, 2, 1), (1, 8, 2, 200)):
         _run(gpu_lib, B, Hq, Hkv, S, score_mod, mask)
@@ -46,6 +66,13 @@ def test_bwd_parity(gpu_lib, score_mod, mask):
 def test_bwd_longer(gpu_lib):
     _run(gpu_lib, 2, 8, 2, 1024, "softcap", "causal")
     _run(gpu_lib, 1, 4, 4, 777, "none", "none")
+
+
+@pytest.mark.parametrize("mask", ["sliding_window", "prefix_lm", "document"])
+def test_bwd_longer_masks(gpu_lib, mask):
+    """S = 1000 and 1024 (window 256, several 128-key tiles per document), MHA and GQA."""
+    _run(gpu_lib, 2, 4, 2, 1024, "softcap", mask)
+    _run(gpu_lib, 1, 4, 4, 1000, "alibi", mask)
 
 
 def test_bwd_deterministic(gpu_lib):
@@ -58,7 +85,8 @@ def test_bwd_deterministic(gpu_lib):
         assert torch.equal(r[0][i], r[1][i]) and torch.equal(r[1][i], r[2][i])
 
 
-@pytest.mark.parametrize("score_mod,mask", [("none", "none"), ("softcap", "causal")])
+@pytest.mark.parametrize("score_mod,mask", [("none", "none"), ("softcap", "causal"), ("none", "sliding_window"),
+                                            ("alibi", "prefix_lm"), ("softcap", "document")])
 def test_bwd_benchmark_shape(gpu_lib, score_mod, mask):
     """The benchmark shape (B = 4, H = 16, S = 4096): the GPU computes every
     head; the oracle checks the first two heads of the last batch entry (heads
@@ -67,12 +95,19 @@ def test_bwd_benchmark_shape(gpu_lib, score_mod, mask):
     x = wi.attention_inputs(B, H, H, S, S, D)
     g = wi.normal_bf16(5, (B, H, S, D), 1.0)
     q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    okw, dkw = _mask_kw(mask, B, S)
     kw = dict(score_mod=score_mod, mask=mask, softcap=20.0)
-    out, lse = gpu_lib.attn_fwd(q, k, v, return_lse=True, **kw)
-    dq, dk, dv = gpu_lib.attn_bwd(q, k, v, dout, lse, **kw)
+    out, lse = gpu_lib.attn_fwd(q, k, v, return_lse=True, **kw, **dkw)
+    dq, dk, dv = gpu_lib.attn_bwd(q, k, v, dout, lse, **kw, **dkw)
     torch.cuda.synchronize()
     sl = (slice(B - 1, B), slice(0, 2))
-    rq, rk, rv = oracle.attention_backward(f64(x["q"][sl]), f64(x["k"][sl]), f64(x["v"][sl]), f64(g[sl]), **kw)
+    if "doc_id" in okw:
+        okw["doc_id"] = okw["doc_id"][B - 1:B]
+    # the oracle sees heads 0-1 as a 2-head problem: ALiBi slopes 2^(-8(h+1)/16)
+    # are 2^(-mb(h+1)/2) with mb = 8 * 2 / 16
+    okw["alibi_max_bias"] = 8.0 * 2 / H
+    rq, rk, rv = oracle.attention_backward(f64(x["q"][sl]), f64(x["k"][sl]), f64(x["v"][sl]), f64(g[sl]), **kw,
+                                           **okw)
     what = f"bwd {score_mod}/{mask} B{B} H{H} S{S} (batch {B - 1}, heads 0-1)"
     assert_close(dq[sl].float().cpu().numpy(), rq, what + " dq")
     assert_close(dk[sl].float().cpu().numpy(), rk, what + " dk")
