@@ -8,7 +8,9 @@
 // are the last Sq positions of its Skv keys (absolute position
 // Skv - Sq + q), which is where the causal mask and the ALiBi distances are
 // measured from.  The arithmetic per score is the prefill kernel's (same
-// score modifiers, same exponent-reference schemes, fp32 accumulation).
+// score modifiers, same exponent-reference schemes, fp32 accumulation); the
+// row sums add the fp32 exponentials (this kernel is bound by memory, so the
+// exact log-sum-exp costs nothing).
 //
 // Mapping onto CDNA4 (memory-bound: every K/V byte is read once, the
 // matrix work is small):
@@ -201,18 +203,18 @@ __global__ __launch_bounds__(NT, (PAGED ? 2 : 3)) void attn_decode_kernel(const 
     // ---- exponent reference and exponentials (the prefill kernel's schemes)
     bf16x8 pb[NPS];
     if constexpr (SM == SM_NONE) {
-      float tsum = exp_pack_sum<NKB, 0>(s, a.c, st.m_sub, pb);
+      float tsum = exp_pack_sum<NKB, 0, true>(s, a.c, st.m_sub, pb);
       if (any_lane(tsum > kOptBound || st.m_ref == neg_inf())) {
         st.template raise<NDB>(xhalf_max(block_max<NKB>(s)) * a.c, o);
-        tsum = exp_pack_sum<NKB, 0>(s, a.c, st.m_sub, pb);
+        tsum = exp_pack_sum<NKB, 0, true>(s, a.c, st.m_sub, pb);
       }
       st.l += tsum;
     } else if constexpr (SM == SM_SOFTCAP_FIXED) {
-      st.l += exp_pack_sum<NKB, 2>(s, a.c, st.m_sub, pb);
+      st.l += exp_pack_sum<NKB, 2, true>(s, a.c, st.m_sub, pb);
     } else {  // ALiBi, softcap with a large cap: lazy rescale on the tile max
       const float hmax = block_max<NKB>(s);
       if (any_lane(hmax > st.thr)) st.template raise<NDB>(xhalf_max(hmax), o);
-      st.l += exp_pack_sum<NKB, 1>(s, a.c, st.m_sub, pb);
+      st.l += exp_pack_sum<NKB, 1, true>(s, a.c, st.m_sub, pb);
     }
     // ---- O^T += V^T P^T
 #pragma unroll

@@ -35,7 +35,8 @@
 //    otherwise the exponentials stay below 256 and no rescale is paid.  The
 //    result is the same softmax: every exponential and the sum share one
 //    reference.  The row sum adds the bf16-rounded probabilities, exactly the
-//    values the PV product consumes.
+//    values the PV product consumes; calls that ask for the log-sum-exp add
+//    the fp32 exponentials instead, so that it is exact to fp32 rounding.
 //  * Masks are analytic: each workgroup computes the KV tile range that
 //    holds any visible key (document masks: two 64-way wave searches over
 //    the doc-id row), each wave classifies every tile as skipped, full (no
@@ -66,7 +67,9 @@ constexpr int min_waves() {
   return attn_qb(D, SM, MK) == 2 || D == 128 || ((SM == SM_TBIAS || SM == SM_BIAS) && D == 64) ? 2 : 3;
 }
 
-template <int D, int SM, int MK>
+// EXACT: the row sums add the fp32 exponentials (calls that ask for lse), else
+// their bf16 copies (see exp_pack_sum).
+template <int D, int SM, int MK, bool EXACT>
 __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int QB = attn_qb(D, SM, MK);  // 32-row query blocks per wave
   constexpr int BM = attn_bm(D, SM, MK);  // query rows per workgroup
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       bool redo = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], cexp, st[qb].m_sub, pb[qb]);
+        tsum[qb] = exp_pack_sum<NKB, MODE, EXACT>(s[qb], cexp, st[qb].m_sub, pb[qb]);
         redo |= (tsum[qb] > kOptBound) || (st[qb].m_ref == neg_inf());
       }
       if (any_lane(redo)) {
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         for (int qb = 0; qb < QB; ++qb) {
           const float rmax = xhalf_max(block_max<NKB>(s[qb]));
           st[qb].template raise<NDB>(rmax * cexp, o[qb]);
-          tsum[qb] = exp_pack_sum<NKB, MODE>(s[qb], cexp, st[qb].m_sub, pb[qb]);
+          tsum[qb] = exp_pack_sum<NKB, MODE, EXACT>(s[qb], cexp, st[qb].m_sub, pb[qb]);
         }
       }
 #pragma unroll
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
         }
       }
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE>(s[qb], a.c, st[qb].m_sub, pb[qb]);
+      for (int qb = 0; qb < QB; ++qb) st[qb].l += exp_pack_sum<NKB, MODE, EXACT>(s[qb], a.c, st[qb].m_sub, pb[qb]);
     }
 
     if constexpr (kPrioExp) __builtin_amdgcn_s_setprio(0);
@@ -725,22 +728,28 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   }
 }
 
-template <int D, int SM, int MK>
+template <int D, int SM, int MK, bool EXACT = false>
 hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, SM, MK>), dim3(a.total), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, SM, MK, EXACT>), dim3(a.total), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int SM>
-hipError_t launch_mask(const AttnArgs& a, int mask, hipStream_t stream) {
+template <int D, int SM, bool EXACT>
+hipError_t launch_mask_x(const AttnArgs& a, int mask, hipStream_t stream) {
   switch (mask) {
-    case MK_NONE: return launch_one<D, SM, MK_NONE>(a, stream);
-    case MK_CAUSAL: return launch_one<D, SM, MK_CAUSAL>(a, stream);
-    case MK_WINDOW: return launch_one<D, SM, MK_WINDOW>(a, stream);
-    case MK_PREFIX: return launch_one<D, SM, MK_PREFIX>(a, stream);
-    case MK_DOC: return launch_one<D, SM, MK_DOC>(a, stream);
+    case MK_NONE: return launch_one<D, SM, MK_NONE, EXACT>(a, stream);
+    case MK_CAUSAL: return launch_one<D, SM, MK_CAUSAL, EXACT>(a, stream);
+    case MK_WINDOW: return launch_one<D, SM, MK_WINDOW, EXACT>(a, stream);
+    case MK_PREFIX: return launch_one<D, SM, MK_PREFIX, EXACT>(a, stream);
+    case MK_DOC: return launch_one<D, SM, MK_DOC, EXACT>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// calls that ask for lse take the exact-sum instantiations
+template <int D, int SM>
+hipError_t launch_mask(const AttnArgs& a, int mask, hipStream_t stream) {
+  return a.lse != nullptr ? launch_mask_x<D, SM, true>(a, mask, stream) : launch_mask_x<D, SM, false>(a, mask, stream);
 }
 
 template <int D>

@@ -151,9 +151,12 @@ struct RowState {
 
 // p = exp2(s * c - m_sub) (MODE 0), exp2(s - m_sub) (MODE 1) or exp2(s)
 // (MODE 2) for the registers of NB S^T blocks, packed to bf16 P^T operands
-// pb[2*NB]; returns this lane's sum of the bf16 values.  The sum runs in four
-// independent partial accumulators so the dot2 chain does not serialise.
-template <int NB, int MODE>
+// pb[2*NB]; returns this lane's sum of the bf16 values (EXACT = false: the
+// normaliser then equals what the PV product consumes) or of the fp32 values
+// (EXACT = true: one more add per two scores, and a log-sum-exp exact to fp32
+// rounding).  The sum runs in four independent partial accumulators so the
+// chain does not serialise.
+template <int NB, int MODE, bool EXACT = false>
 __device__ __forceinline__ float exp_pack_sum(const f32x16* s, float c, float m_sub, bf16x8* pb) {
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -168,8 +171,13 @@ __device__ __forceinline__ float exp_pack_sum(const f32x16* s, float c, float m_
         x0 -= m_sub;
         x1 -= m_sub;
       }
-      const bf16x2 pp = {(bf16)exp2_fast(x0), (bf16)exp2_fast(x1)};
-      acc[(j >> 1) & 3] = add_bf16_pair(pp, acc[(j >> 1) & 3]);
+      const float e0 = exp2_fast(x0), e1 = exp2_fast(x1);
+      const bf16x2 pp = {(bf16)e0, (bf16)e1};
+      if constexpr (EXACT) {
+        acc[(j >> 1) & 3] += e0 + e1;
+      } else {
+        acc[(j >> 1) & 3] = add_bf16_pair(pp, acc[(j >> 1) & 3]);
+      }
       pb[kb * 2 + (j >> 3)][j & 7] = pp[0];
       pb[kb * 2 + (j >> 3)][(j & 7) + 1] = pp[1];
     }

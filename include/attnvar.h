@@ -116,10 +116,12 @@ typedef struct {
  *   q   [B, Hq,  Sq,  D]    k [B, Hkv, Skv, D]    v [B, Hkv, Skv, D]
  *   out [B, Hq,  Sq,  D]    written (bf16, round-to-nearest-even from fp32)
  *   lse [B, Hq,  Sq]  fp32  natural-log sum-exp of the modified, masked
- *                           scores per row; may be NULL (not written).  The
- *                           row sum adds the bf16-rounded probabilities that
- *                           the PV product consumes, so lse is within
- *                           ln(1 + 2^-8) = 3.9e-3 of the exact value.
+ *                           scores per row; may be NULL (not written).  When
+ *                           it is requested the row sums add the fp32
+ *                           exponentials (lse exact to fp32 rounding, one more
+ *                           add per two scores); without it they add the
+ *                           bf16-rounded probabilities that the PV product
+ *                           consumes.  Either sum normalises out.
  * Query head h reads key/value head h / (Hq / Hkv).  D in {32, 64, 128}.
  * Sq == 0 launches nothing; Skv == 0 writes zero rows and lse = -inf.
  * Pointers of empty tensors may be NULL (q/out when Sq == 0, k/v when Skv == 0).

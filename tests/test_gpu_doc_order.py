@@ -111,4 +111,4 @@ def test_fwd_with_order_against_oracle(gpu_lib):
     ref, ref_lse = oracle.attention(f64(x["q"]), f64(x["k"]), f64(x["v"]), mask="document",
                                     doc_id=doc.cpu().numpy())
     assert_close(out.float().cpu().numpy(), ref, "document with order")
-    assert_close(lse.cpu().numpy(), ref_lse, "document with order lse", atol=4e-3, rtol=1e-5)
+    assert_close(lse.cpu().numpy(), ref_lse, "document with order lse", atol=1e-3, rtol=1e-5)
