@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["attnvar_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "diff_attn_fwd.hip", "evoformer.hip", "doc_order.hip"]
+SOURCES = ["attnvar_api.cpp", "attn_fwd.hip", "attn_decode.hip", "attn_bwd.hip", "diff_attn_fwd.hip", "evoformer.hip",
+           "evo_fused.hip", "doc_order.hip"]
 OUT = os.path.join(HERE, "libattnvar.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

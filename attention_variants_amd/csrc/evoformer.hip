@@ -388,6 +388,7 @@ hipError_t launch_evo_proj(const EvoArgs& a, hipStream_t stream) {
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh) { return (size_t)4 * Ns * Nr * H * dh * 2; }
 
 hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream) {
+  if (evo_fused_fits(a)) return launch_evo_fused(a, stream);
   hipError_t e = a.dh == 64 ? launch_evo_proj<64>(a, stream) : launch_evo_proj<32>(a, stream);
   if (e != hipSuccess) return e;
 

@@ -274,7 +274,9 @@ int diff_head_fwd(const void* q, const void* k, const void* v, const float* lamb
  * The projections are computed into `workspace` (bf16, owned by the caller,
  * at least evoformer_workspace_bytes(...) bytes, 256-byte aligned) by one
  * kernel, then consumed by the attention kernel; the q plane holds scale*q
- * (the softmax scale applied before the bf16 rounding).  scale = 0 selects
+ * (the softmax scale applied before the bf16 rounding).  With Cm = 256 and
+ * Nr <= 256, Nr a multiple of 8, one kernel keeps the projections on chip
+ * and leaves the workspace untouched (it is still required).  scale = 0 selects
  * 1/sqrt(dh).  Supported: dh in {32, 64} (the AlphaFold2 8 heads x 32 and the talk
  * notes' kernel-benchmark 4 heads x 64), Cm a multiple of 64, H*dh a multiple
  * of 128. */

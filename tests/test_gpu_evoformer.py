@@ -119,3 +119,41 @@ def test_pair_bias_minus_inf(gpu_lib):
     got = out.float().cpu().numpy()
     assert np.isfinite(got).all()
     assert_close(got, ref, "evoformer pair bias with -inf")
+
+
+# Shapes that take the single-launch form (Cm = 256, N_res a multiple of 8,
+# up to 256 residues, dh 32 or 64): every residue block count, odd and even,
+# ragged last 64-key tiles, waves with no block, one block or two; and just
+# past the limit (the two launches).
+FUSED = [(8, 32, 8), (24, 32, 4), (64, 32, 8), (96, 64, 4), (200, 32, 8), (232, 64, 4), (256, 64, 4),
+         (256, 32, 8), (264, 32, 8), (392, 32, 4)]
+
+
+@pytest.mark.parametrize("Nr,dh,H", FUSED)
+def test_fused_form_all_rows(gpu_lib, Nr, dh, H):
+    _run(gpu_lib, 2, Nr, Cm=256, H=H, dh=dh)
+
+
+def test_fused_form_pair_bias_minus_inf(gpu_lib):
+    """As test_pair_bias_minus_inf, on the single-launch form."""
+    Ns, Nr, Cm, H, dh = 3, 136, 256, 8, 32
+    x = wi.evoformer_inputs(Ns, Nr, Cm, H, dh)
+    drop = np.random.default_rng(42).random((H, Nr, Nr)) < 0.35
+    drop[:, np.arange(Nr), np.arange(Nr)] = False
+    x["bias"] = np.where(drop, np.uint16(0xFF80), x["bias"]).astype(np.uint16)
+    t = {n: to_dev(x[n]) for n in x}
+    out = gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=H, dh=dh)
+    torch.cuda.synchronize()
+    ref = oracle.evoformer_row_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]), f64(x["wg"]),
+                                               f64(x["bias"]), H=H, dh=dh)
+    got = out.float().cpu().numpy()
+    assert np.isfinite(got).all()
+    assert_close(got, ref, "evoformer single-launch form, pair bias with -inf")
+
+
+def test_fused_form_deterministic(gpu_lib):
+    x = wi.evoformer_inputs(4, 248, 256, 8, 32)
+    t = {n: to_dev(x[n]) for n in x}
+    r = [gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=8, dh=32)
+         for _ in range(3)]
+    assert torch.equal(r[0], r[1]) and torch.equal(r[1], r[2])
