@@ -662,13 +662,19 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
     }
   }
 
-  // ---- epilogue: O / l, bf16 store (staged through LDS), optional LSE
+  // ---- epilogue: O / l, bf16 store (staged through LDS), optional LSE.
+  // The lane-derived values come from an opaque copy of the thread id: the
+  // compiler would otherwise keep the prologue's copies (the Q row offsets
+  // in LDS, the lane id) alive across the key loop, and spill them.
   if constexpr (kStageQO) __syncthreads();  // every wave is done with the K/V tiles
+  int tid_e = tid;
+  asm volatile("" : "+v"(tid_e));
+  const int hh_e = (tid_e >> 5) & 1, l32_e = tid_e & 31;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = xhalf_sum(st[qb].l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    const int q = qi[qb];
+    const int q = qw + 32 * qb + l32_e;
     if (q >= a.Sq) continue;
     if constexpr (kGated) {
       // Evoformer: out[token, hq*D + d] = sigmoid(gate[b, hq, q, d]) * O[d] / l with
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = db * 32 + 8 * g4 + 4 * hh;
+          const int d0 = db * 32 + 8 * g4 + 4 * hh_e;
           const bf16x4 gv = gate[qb][db * 4 + g4];
           bf16x4 val;
 #pragma unroll
@@ -700,25 +706,20 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
           bf16x4 val;
 #pragma unroll
           for (int e = 0; e < 4; ++e) val[e] = (bf16)(o[qb][db][g4 * 4 + e] * inv);
-          *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh) = val;
+          *(bf16x4*)(orow + db * 32 + 8 * g4 + 4 * hh_e) = val;
         }
       }
-      if (a.lse != nullptr && hh == 0) {
+      if (a.lse != nullptr && hh_e == 0) {
         a.lse[((size_t)b * a.Hq + hq) * a.Sq + q] =
             l_tot > 0.f ? (st[qb].m_ref + __log2f(l_tot)) * kLn2 : neg_inf();
       }
     }
   }
   if constexpr (kStageQO) {
-    // O tile: rows q0 .. q0+BM-1 of the (b, hq) slice, contiguous in memory.
-    // The offsets are those of the Q tile load; with a score modifier, an
-    // opaque copy of the thread id keeps the compiler from computing them
-    // once before the key loop and spilling them across it (vanilla has the
-    // registers to hold them, and runs faster with its own schedule).
+    // O tile: rows q0 .. q0+BM-1 of the (b, hq) slice, contiguous in memory,
+    // at the offsets of the Q tile load (recomputed from the opaque thread id)
     __syncthreads();
     bf16* obase = (bf16*)a.o + qoff;
-    int tid_e = tid;
-    if constexpr (SM != SM_NONE) asm volatile("" : "+v"(tid_e));
 #pragma unroll
     for (int c = 0; c < QCH; ++c) {
       const int idx = tid_e + NT * c;
