@@ -24,7 +24,11 @@
 //  2. dK and dV by workgroups that own a 128-key tile and stream the query
 //     tiles of every query head of the KV head;
 //  3. dQ by workgroups that own 128 query rows and stream the key tiles.
+// P and dS enter the gradient products rounded to bf16, plus their rounding
+// residue as a second bf16 operand in the blocks that hold large values.
 // No atomics: every output element has one writer (deterministic).
+
+#include <type_traits>
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
@@ -37,6 +41,13 @@ constexpr int D = 64;
 constexpr int NDS = D / 16;   // k-steps over the head dimension
 constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
 constexpr int CPR = D / 8;    // 16-byte chunks per row
+// A 32 x 32 block of P (or dS) whose largest magnitude exceeds this feeds its
+// gradient product as a bf16 hi + lo pair, other blocks as bf16 alone.  A
+// dropped residue is at most 2^-9 of its operand, so under 2^-12 in absolute
+// terms; its sign follows the inputs, so over N products the sum grows like
+// sqrt(N).  Concentrated attention (P near 1 over many queries, the case
+// the pairs exist for) always takes the pair.
+constexpr float kLoThresh = 0.125f;
 
 // Score pieces shared by both gradient kernels, for one element: raw q.k in
 // `s`, query position qp, key position kp.  Returns p = exp(t - lse) (0 when
@@ -64,6 +75,19 @@ __device__ __forceinline__ bool bwd_visible(const BwdArgs& a, int q, int kp, int
   if constexpr (MK == MK_PREFIX) return kp < a.prefix || kp <= q;
   if constexpr (MK == MK_DOC) return qd == kd;
   return true;
+}
+
+// Whether every key n0..n1 of a tile is visible to every query qw..qwlast of
+// a wave (the forward's full-tile classes); kdoc = the tile's key document ids.
+template <int MK>
+__device__ __forceinline__ bool bwd_tile_full(const BwdArgs& a, int n0, int n1, int qw, int qwlast, const int* kdoc,
+                                              int qd_lo, int qd_hi) {
+  bool full = n1 < a.Skv;
+  if constexpr (MK == MK_CAUSAL) full &= n1 <= qw;
+  if constexpr (MK == MK_WINDOW) full &= n1 <= qw && qwlast - n0 < a.window;
+  if constexpr (MK == MK_PREFIX) full &= n1 < a.prefix || n1 <= qw;
+  if constexpr (MK == MK_DOC) full &= kdoc[0] == qd_lo && kdoc[n1 - n0] == qd_lo && qd_lo == qd_hi;
+  return full;
 }
 
 // ---------------------------------------------------------------------------
@@ -211,6 +235,20 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
         skip |= kd_hi < qd_lo || (kd_lo > qd_hi && qd_hi >= 0);
       }
       if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+      // full block: every live key of the wave is visible to every query of
+      // the block, so no element mask (keys past Skv are never stored, rows
+      // past Sq have p = 0 from their +inf reference)
+      bool full = true;
+      if constexpr (MK == MK_CAUSAL) {
+        full = kwlast <= qb0;
+      } else if constexpr (MK == MK_WINDOW) {
+        full = kwlast <= qb0 && qblast - kw0 < a.window;
+      } else if constexpr (MK == MK_PREFIX) {
+        full = kwlast < a.prefix || kwlast <= qb0;
+      } else if constexpr (MK == MK_DOC) {
+        full = kd_lo == kd_hi && Dq[buf][32 * blk] == kd_lo && Dq[buf][32 * blk + 31] == kd_lo;
+      }
+      full = __builtin_amdgcn_readfirstlane((int)full) != 0;
       // S = Q K^T, dP = dO V^T: lane = key, registers = queries qb0 + 8(j/4) + 4hh + j%4
       f32x16 sc = {}, dp = {};
 #pragma unroll
@@ -219,45 +257,78 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
         sc = mfma32(*(const bf16x8*)&Qs[buf][off], kreg[s], sc);
         dp = mfma32(*(const bf16x8*)&Gs[buf][off], vreg[s], dp);
       }
-      bf16x8 phi[2], plo[2], dhi[2], dlo[2];
+      float pv[16], dsv[16], dmv[16];
+      bf16x8 phi[2], dhi[2];
+      float pmax = 0.f, dsmax = 0.f;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 l4 = *(const f32x4*)&Ls[buf][32 * blk + 8 * g4 + 4 * hh];
-        const f32x4 e4 = *(const f32x4*)&Es[buf][32 * blk + 8 * g4 + 4 * hh];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = 4 * g4 + e;
           const int q = qb0 + 8 * g4 + 4 * hh + e;
           const float bias = SM == SM_ALIBI ? slope2 * (float)(key - q) : 0.f;
-          float dmod;
-          float p = bwd_prob<SM>(a, sc[j], l4[e], bias, dmod);
-          const int qd = kDoc ? Dq[buf][32 * blk + 8 * g4 + 4 * hh + e] : 0;
-          const bool ok = key_live && bwd_visible<MK>(a, q, key, qd, kdoc);
-          p = ok ? p : 0.f;
-          const float ds = p * (dp[j] - e4[e]) * dmod;
-          const bf16 ph = (bf16)p;
-          phi[j >> 3][j & 7] = ph;
-          plo[j >> 3][j & 7] = (bf16)(p - (float)ph);
-          const bf16 hi = (bf16)ds;
-          dhi[j >> 3][j & 7] = hi;
-          dlo[j >> 3][j & 7] = (bf16)(ds - (float)hi);
+          pv[j] = bwd_prob<SM>(a, sc[j], l4[e], bias, dmv[j]);
         }
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (query k-steps in the register order).
-      // P and dS enter as bf16 hi + lo pairs: the sums over queries cancel
-      // strongly where attention concentrates, and one bf16 rounding of the
-      // operand would show in the result.
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = 8 * (j >> 2) + 4 * hh + (j & 3);
+          const int qd = kDoc ? Dq[buf][32 * blk + r] : 0;
+          pv[j] = bwd_visible<MK>(a, qb0 + r, key, qd, kdoc) ? pv[j] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 e4 = *(const f32x4*)&Es[buf][32 * blk + 8 * g4 + 4 * hh];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 4 * g4 + e;
+          const float p = pv[j];
+          const float ds = p * (dp[j] - e4[e]) * dmv[j];
+          dsv[j] = ds;
+          pmax = fmaxf(pmax, p);
+          dsmax = fmaxf(dsmax, fabsf(ds));
+          phi[j >> 3][j & 7] = (bf16)p;
+          dhi[j >> 3][j & 7] = (bf16)ds;
+        }
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (query k-steps in the register order),
+      // with P and dS rounded to bf16 ...
 #pragma unroll
       for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          const bf16x8 gt_ = vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl);
-          dvT[d2] = mfma32(gt_, phi[tt], dvT[d2]);
-          dvT[d2] = mfma32(gt_, plo[tt], dvT[d2]);
-          const bf16x8 qt_ = vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl);
-          dkT[d2] = mfma32(qt_, dhi[tt], dkT[d2]);
-          dkT[d2] = mfma32(qt_, dlo[tt], dkT[d2]);
+          dvT[d2] = mfma32(vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl), phi[tt], dvT[d2]);
+          dkT[d2] = mfma32(vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl), dhi[tt], dkT[d2]);
         }
+      // ... plus their rounding residues (the bf16 lo halves) where the block
+      // holds a large value: where attention concentrates, the sums over
+      // queries of nearly equal P (or dS) cancel the random signs of the
+      // inputs, and one bf16 rounding would show in the result.  Below the
+      // threshold the residue is under kLoThresh * 2^-9 per product.
+      const bool lo_p = any_lane(pmax > kLoThresh), lo_ds = any_lane(dsmax > kLoThresh);
+      if (lo_p) {
+        bf16x8 plo[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) plo[j >> 3][j & 7] = (bf16)(pv[j] - (float)phi[j >> 3][j & 7]);
+#pragma unroll
+        for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            dvT[d2] = mfma32(vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl), plo[tt], dvT[d2]);
+      }
+      if (lo_ds) {
+        bf16x8 dlo[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dlo[j >> 3][j & 7] = (bf16)(dsv[j] - (float)dhi[j >> 3][j & 7]);
+#pragma unroll
+        for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            dkT[d2] = mfma32(vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl), dlo[tt], dkT[d2]);
+      }
     }
   }
 
@@ -281,13 +352,209 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row statistics (launch 1).  Workgroup = 256 query rows of one (b, query
+// head), wave = 64 rows as two 32-row blocks in the forward's layout:
+// S^T = K Q^T and dP^T = V dO^T with Q and dO in registers (lane = query),
+// so each K and V fragment read from LDS feeds the MFMAs of both blocks.
+// K and V are only read as rows here, so both tiles use the forward's padded
+// row pitch.  With the forward's lse only as an exponent reference, the
+// pass sums l = sum p and sum p dP per row, p = exp(t - lse).
+template <int SM, int MK>
+__global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) {
+  constexpr int BN = 64;
+  constexpr int QB = 2;
+  constexpr int BM = 4 * 32 * QB;
+  constexpr int NCH = BN * CPR / NT;
+  constexpr int KP = D + 8;
+  constexpr bool kDoc = MK == MK_DOC;
+  constexpr bool kWeighted = MK == MK_CAUSAL || MK == MK_PREFIX;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) int Dk[2][kDoc ? BN : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int nM = (a.Sq + BM - 1) / BM;
+  int mt_lin, bh;
+  if constexpr (kWeighted) {
+    const TileIdx ti = weighted_tile(blockIdx.x, gridDim.x, nM);
+    mt_lin = ti.mt_lin;
+    bh = ti.bh;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    mt_lin = L % nM;
+    bh = L / nM;
+  }
+  const int hq = bh % a.Hq, b = bh / a.Hq;
+  const int hk = hq / a.g;
+  const int mt = kWeighted ? nM - 1 - mt_lin : mt_lin;
+  const int q0 = mt * BM;
+  const int qw = q0 + 32 * QB * __builtin_amdgcn_readfirstlane(w);
+  int qi[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qi[qb] = qw + 32 * qb + l32;
+  const size_t qoff = ((size_t)b * a.Hq + hq) * (size_t)a.Sq * D;
+  const size_t kvoff = ((size_t)b * a.Hkv + hk) * (size_t)a.Skv * D;
+  const auto qrs = make_rsrc((const bf16*)a.q + qoff, (uint32_t)a.Sq * D * 2);
+  const auto grs = make_rsrc((const bf16*)a.dout + qoff, (uint32_t)a.Sq * D * 2);
+  const auto krs = make_rsrc((const bf16*)a.k + kvoff, (uint32_t)a.Skv * D * 2);
+  const auto vrs = make_rsrc((const bf16*)a.v + kvoff, (uint32_t)a.Skv * D * 2);
+  // rows past Sq read as zero (buffer bounds) and are never stored
+  bf16x8 qreg[QB][NDS], greg[QB][NDS];
+  float l2[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      const uint32_t off = (uint32_t)(qi[qb] * D + s * 16 + hh * 8) * 2;
+      qreg[qb][s] = __builtin_bit_cast(bf16x8, buf_load16(qrs, off));
+      greg[qb][s] = __builtin_bit_cast(bf16x8, buf_load16(grs, off));
+    }
+    l2[qb] = qi[qb] < a.Sq ? a.lse[((size_t)b * a.Hq + hq) * a.Sq + qi[qb]] * kLog2e : __builtin_inff();
+  }
+  const float slope2 = SM == SM_ALIBI ? uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq)) : 0.f;
+
+  // the forward's analytic key range of the query tile [q0, qlast]
+  const int nKV = (a.Skv + BN - 1) / BN;
+  const int qlast = min(q0 + BM - 1, a.Sq - 1);
+  const int qwlast = min(qw + 32 * QB - 1, a.Sq - 1);
+  const int* docrow = kDoc ? a.doc + (size_t)b * a.Sq : nullptr;
+  int n_lo = 0, n_hi = nKV;
+  int qdoc[QB] = {};
+  int qd_lo = 0, qd_hi = 0;
+  if constexpr (MK == MK_CAUSAL) {
+    n_hi = min(nKV, qlast / BN + 1);
+  } else if constexpr (MK == MK_WINDOW) {
+    n_lo = max(0, q0 - a.window + 1) / BN;
+    n_hi = min(nKV, qlast / BN + 1);
+  } else if constexpr (MK == MK_PREFIX) {
+    n_hi = min(nKV, max(a.prefix - 1, qlast) / BN + 1);
+  } else if constexpr (MK == MK_DOC) {
+    const int kstart = wave_lower_bound(docrow, a.Skv, docrow[q0]);
+    const int kend = wave_upper_bound(docrow, a.Skv, docrow[qlast]);
+    n_lo = kstart / BN;
+    n_hi = min(nKV, (kend + BN - 1) / BN);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) qdoc[qb] = docrow[min(qi[qb], a.Sq - 1)];
+    qd_lo = __builtin_amdgcn_readfirstlane(docrow[min(qw, a.Sq - 1)]);
+    qd_hi = __builtin_amdgcn_readfirstlane(docrow[max(qwlast, 0)]);
+  }
+
+  i32x4 kr[NCH], vr[NCH];
+  int dr = 0;
+  auto gload = [&](int nt) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + NT * c;
+      const uint32_t off = (uint32_t)((nt * BN + idx / CPR) * D + (idx % CPR) * 8) * 2;
+      kr[c] = buf_load16(krs, off);
+      vr[c] = buf_load16(vrs, off);
+    }
+    if constexpr (kDoc) {
+      if (tid < BN) {
+        const int kp = nt * BN + tid;
+        dr = kp < a.Skv ? docrow[kp] : 0x7fffffff;
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int idx = tid + NT * c;
+      const int off = (idx / CPR) * KP + (idx % CPR) * 8;
+      *(i32x4*)&Ks[buf][off] = kr[c];
+      *(i32x4*)&Vs[buf][off] = vr[c];
+    }
+    if constexpr (kDoc) {
+      if (tid < BN) Dk[buf][tid] = dr;
+    }
+  };
+
+  float psum[QB] = {}, pdsum[QB] = {};  // this lane's half of each row
+  if (n_lo < n_hi) gload(n_lo);
+  for (int nt = n_lo; nt < n_hi; ++nt) {
+    const int buf = (nt - n_lo) & 1;
+    sstore(buf);
+    __syncthreads();
+    if (nt + 1 < n_hi) gload(nt + 1);
+    const int n0 = nt * BN, n1 = n0 + BN - 1;
+    // skip the tile when none of its keys is visible to this wave's queries
+    bool skip = qw >= a.Sq;
+    if constexpr (MK == MK_CAUSAL) {
+      skip |= n0 > qwlast;
+    } else if constexpr (MK == MK_WINDOW) {
+      skip |= n0 > qwlast || qw - n1 >= a.window;
+    } else if constexpr (MK == MK_PREFIX) {
+      skip |= n0 >= a.prefix && n0 > qwlast;
+    } else if constexpr (MK == MK_DOC) {
+      skip |= Dk[buf][BN - 1] < qd_lo || Dk[buf][0] > qd_hi;
+    }
+    if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+    const bool full = __builtin_amdgcn_readfirstlane((int)bwd_tile_full<MK>(a, n0, n1, qw, qwlast, Dk[buf], qd_lo, qd_hi)) != 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T, dP^T of 32 keys: registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
+      f32x16 sc[QB], dp[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb] = dp[qb] = f32x16{};
+      const bf16* krow = Ks[buf] + (kb * 32 + l32) * KP + hh * 8;
+      const bf16* vrow = Vs[buf] + (kb * 32 + l32) * KP + hh * 8;
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        const bf16x8 kf = *(const bf16x8*)(krow + s * 16);
+        const bf16x8 vf = *(const bf16x8*)(vrow + s * 16);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sc[qb] = mfma32(kf, qreg[qb][s], sc[qb]);
+          dp[qb] = mfma32(vf, greg[qb][s], dp[qb]);
+        }
+      }
+      // the element mask only on tiles that are not full (two copies of the
+      // accumulation, so that full tiles carry no mask registers)
+      auto accumulate = [&](auto masked) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int ko = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+            const float bias = SM == SM_ALIBI ? slope2 * (float)(n0 + ko - qi[qb]) : 0.f;
+            float dmod;
+            float p = bwd_prob<SM>(a, sc[qb][j], l2[qb], bias, dmod);
+            if constexpr (decltype(masked)::value) {
+              const int kd = kDoc ? Dk[buf][ko] : 0;
+              p = n0 + ko < a.Skv && bwd_visible<MK>(a, qi[qb], n0 + ko, qdoc[qb], kd) ? p : 0.f;
+            }
+            psum[qb] += p;
+            pdsum[qb] = fmaf(p, dp[qb][j], pdsum[qb]);
+          }
+      };
+      if (full) {
+        accumulate(std::false_type{});
+      } else {
+        accumulate(std::true_type{});
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one 32-key block of S and dP live at a time
+    }
+  }
+
+  // corrected reference lse + log2(l) (log2 units) and Delta = sum p dP / l
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lsum = xhalf_sum(psum[qb]), dsum = xhalf_sum(pdsum[qb]);
+    if (qi[qb] < a.Sq && hh == 0) {
+      const size_t r = ((size_t)b * a.Hq + hq) * a.Sq + qi[qb];
+      a.stats[2 * r] = lsum > 0.f ? l2[qb] + __log2f(lsum) : __builtin_inff();
+      a.stats[2 * r + 1] = lsum > 0.f ? dsum / lsum : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ.  Workgroup = 128 query rows of one (b, query head), wave = 32 rows;
 // the forward's layout: S^T = K Q^T and dP^T = V dO^T with Q, dO held in
 // registers (lane = query), K and V tiles staged in LDS (swizzled), then
 // dQ^T += K^T dS^T with K^T read transposed.
-// STATS = true is launch 1 (row statistics): the same loop without the dQ
-// product, summing p and p * dP per row.
-template <int SM, int MK, bool STATS>
+template <int SM, int MK>
 __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   constexpr int BN = 64;
   constexpr int NCH = BN * CPR / NT;
@@ -330,18 +597,12 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   }
   const bool q_live = q < a.Sq;
   const size_t rrow = ((size_t)b * a.Hq + hq) * a.Sq + (q_live ? q : 0);
-  // exponent reference (log2 units) and Delta: the forward's lse in the
-  // statistics pass, the corrected pair afterwards
+  // exponent reference (log2 units) and Delta from the statistics pass
   float l2 = __builtin_inff(), dl = 0.f;
   if (q_live) {
-    if constexpr (STATS) {
-      l2 = a.lse[rrow] * kLog2e;
-    } else {
-      l2 = a.stats[2 * rrow];
-      dl = a.stats[2 * rrow + 1];
-    }
+    l2 = a.stats[2 * rrow];
+    dl = a.stats[2 * rrow + 1];
   }
-  float psum = 0.f, pdsum = 0.f;  // statistics pass: this lane's half of the row
   const float slope2 = SM == SM_ALIBI ? uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq)) : 0.f;
 
   f32x16 dqT[NDB];
@@ -422,6 +683,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
       skip |= Dk[buf][BN - 1] < qd_lo || Dk[buf][0] > qd_hi;
     }
     if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
+    const bool full = __builtin_amdgcn_readfirstlane((int)bwd_tile_full<MK>(a, n0, n1, qw, qwlast, Dk[buf], qd_lo, qd_hi)) != 0;
     // S^T, dP^T: lane = query, registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
     f32x16 sc[2], dp[2];
 #pragma unroll
@@ -434,50 +696,58 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
         dp[kb] = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp[kb]);
       }
     }
-    bf16x8 dhi[4], dlo[4];
+    bf16x8 dhi[4];
+    float dsv[2][16];
+    float dsmax = 0.f;
+    float dmv[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kp = n0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
         const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
-        float dmod;
-        float p = bwd_prob<SM>(a, sc[kb][j], l2, bias, dmod);
-        const int kd = kDoc ? Dk[buf][kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3)] : 0;
-        const bool ok = kp < a.Skv && bwd_visible<MK>(a, q, kp, qdoc, kd);
-        p = ok ? p : 0.f;
-        if constexpr (STATS) {
-          psum += p;
-          pdsum = fmaf(p, dp[kb][j], pdsum);
-        } else {
-          const float ds = p * (dp[kb][j] - dl) * dmod;
-          const bf16 hi = (bf16)ds;
-          dhi[kb * 2 + (j >> 3)][j & 7] = hi;
-          dlo[kb * 2 + (j >> 3)][j & 7] = (bf16)(ds - (float)hi);
-        }
+        dsv[kb][j] = bwd_prob<SM>(a, sc[kb][j], l2, bias, dmv[kb][j]);
       }
-    if constexpr (!STATS) {
-      // dQ^T += K^T dS^T, dS as a bf16 hi + lo pair (the row of dS sums to
-      // zero, so the products cancel)
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ko = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          const int kd = kDoc ? Dk[buf][ko] : 0;
+          dsv[kb][j] = n0 + ko < a.Skv && bwd_visible<MK>(a, q, n0 + ko, qdoc, kd) ? dsv[kb][j] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float ds = dsv[kb][j] * (dp[kb][j] - dl) * dmv[kb][j];
+        dsv[kb][j] = ds;
+        dsmax = fmaxf(dsmax, fabsf(ds));
+        dhi[kb * 2 + (j >> 3)][j & 7] = (bf16)ds;
+      }
+    // dQ^T += K^T dS^T with dS rounded to bf16, plus its rounding residue
+    // (the lo half) where the tile holds a large |dS|: the row of dS sums
+    // to zero, so the products cancel (the threshold as in dK, dV)
+#pragma unroll
+    for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dqT[d2] = mfma32(vt_operand<D>(Ks[buf], t, d2 * 32, tl), dhi[t], dqT[d2]);
+    if (any_lane(dsmax > kLoThresh)) {
+      bf16x8 dlo[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          dlo[kb * 2 + (j >> 3)][j & 7] = (bf16)(dsv[kb][j] - (float)dhi[kb * 2 + (j >> 3)][j & 7]);
 #pragma unroll
       for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const bf16x8 kt_ = vt_operand<D>(Ks[buf], t, d2 * 32, tl);
-          dqT[d2] = mfma32(kt_, dhi[t], dqT[d2]);
-          dqT[d2] = mfma32(kt_, dlo[t], dqT[d2]);
-        }
+        for (int t = 0; t < 4; ++t) dqT[d2] = mfma32(vt_operand<D>(Ks[buf], t, d2 * 32, tl), dlo[t], dqT[d2]);
     }
   }
 
-  if constexpr (STATS) {
-    const float lsum = xhalf_sum(psum), dsum = xhalf_sum(pdsum);
-    if (q_live && hh == 0) {
-      a.stats[2 * rrow] = lsum > 0.f ? l2 + __log2f(lsum) : __builtin_inff();
-      a.stats[2 * rrow + 1] = lsum > 0.f ? dsum / lsum : 0.f;
-    }
-    return;
-  }
   if (!q_live) return;
   bf16* dqrow = (bf16*)a.dq + qoff + (size_t)q * D;
 #pragma unroll
@@ -498,13 +768,14 @@ __global__ __launch_bounds__(NT) void zero_fill_kernel(i32x4* p, size_t n16) {
 
 template <int SM, int MK>
 hipError_t launch_bwd2(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, MK, true>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  const int total_s = a.B * a.Hq * ((a.Sq + 255) / 256);
+  hipLaunchKernelGGL((attn_bwd_stats_kernel<SM, MK>), dim3(total_s), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<SM, MK>), dim3(a.total), dim3(NT), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, MK, false>), dim3(a.total_q), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<SM, MK>), dim3(a.total_q), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

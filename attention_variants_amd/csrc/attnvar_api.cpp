@@ -383,7 +383,7 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return AV_ERR_ALIGN;
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
-  if ((uint64_t)(Sq + 128) * D * 2 > kMaxSliceBytes || (uint64_t)(Skv + 128) * D * 2 > kMaxSliceBytes)
+  if ((uint64_t)(Sq + 256) * D * 2 > kMaxSliceBytes || (uint64_t)(Skv + 128) * D * 2 > kMaxSliceBytes)
     return AV_ERR_TOO_LARGE;
   const int64_t total = (int64_t)B * Hkv * ((Skv + 127) / 128);
   const int64_t total_q = (int64_t)B * Hq * ((Sq + 127) / 128);
