@@ -557,6 +557,19 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "document", "B": B, "H": H, "S": S, "D": D, "launches": steps}))
         return
+    if what in ("window", "causal"):
+        # sliding window 256 (causal) or plain causal at S = 4096, 16 heads
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        mask = "sliding_window" if what == "window" else "causal"
+        torch.cuda.synchronize()
+        for _ in range(steps):
+            av.attn_fwd(q, k, v, mask=mask, window=256, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": what, "B": B, "H": H, "S": S, "D": D, "window": 256, "launches": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -589,7 +602,7 @@ def main():
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
-                                          "document",
+                                          "document", "window", "causal",
                                           "decode", "decode_b1", "bwd", "bias"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
