@@ -493,20 +493,23 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
       //      limits pass through an empty asm so that the compares are not
       //      hoisted out of the branch into every tile.
       if (!full) {
-        int lim = a.Skv - kbase, rel = qi[qb] - kbase, pre = a.prefix - kbase, wlo = rel - a.window;
-        asm volatile("" : "+v"(lim), "+v"(rel), "+v"(pre), "+v"(wlo));
+        // the visible key offsets of this lane's row form one range
+        // (wlo, hi] (the document mask adds its id test): hi = the last key
+        // before Skv, capped at the row's own position for causal masks and
+        // at max(prefix - 1, own position) for PrefixLM
+        const int rel = qi[qb] - kbase;
+        int hi = a.Skv - kbase - 1, wlo = rel - a.window;
+        if constexpr (MK == MK_CAUSAL || MK == MK_WINDOW) hi = min(hi, rel);
+        if constexpr (MK == MK_PREFIX) hi = min(hi, max(a.prefix - kbase - 1, rel));
+        asm volatile("" : "+v"(hi), "+v"(wlo));
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const int off = kb * 32 + 8 * (j >> 2) + (j & 3);
-            bool ok = off < lim;
-            if constexpr (MK == MK_CAUSAL) {
-              ok = ok && (off <= rel);
-            } else if constexpr (MK == MK_WINDOW) {
-              ok = ok && (off <= rel) && (off > wlo);
-            } else if constexpr (MK == MK_PREFIX) {
-              ok = ok && ((off < pre) || (off <= rel));
+            bool ok = off <= hi;
+            if constexpr (MK == MK_WINDOW) {
+              ok = ok && (off > wlo);
             } else if constexpr (MK == MK_DOC) {
               ok = ok && (Ds[buf][off + 4 * hh] == dq[qb]);
             }
