@@ -684,67 +684,62 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
     }
     if (__builtin_amdgcn_readfirstlane((int)skip)) continue;
     const bool full = __builtin_amdgcn_readfirstlane((int)bwd_tile_full<MK>(a, n0, n1, qw, qwlast, Dk[buf], qd_lo, qd_hi)) != 0;
-    // S^T, dP^T: lane = query, registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
-    f32x16 sc[2], dp[2];
+    // one 32-key half of the tile at a time (S, dP, dS and its dQ products),
+    // so that only one half's scores are live
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = dp[kb] = f32x16{};
+      // S^T, dP^T: lane = query, registers = keys n0 + 32 kb + 8(j/4) + 4hh + j%4
+      f32x16 sc = {}, dp = {};
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
         const int off = tr_tile_off<D>(kb * 32 + l32, s * 16 + hh * 8);
-        sc[kb] = mfma32(*(const bf16x8*)&Ks[buf][off], qreg[s], sc[kb]);
-        dp[kb] = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp[kb]);
+        sc = mfma32(*(const bf16x8*)&Ks[buf][off], qreg[s], sc);
+        dp = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp);
       }
-    }
-    bf16x8 dhi[4];
-    float dsv[2][16];
-    float dsmax = 0.f;
-    float dmv[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      float dsv[16], dmv[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kp = n0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
         const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
-        dsv[kb][j] = bwd_prob<SM>(a, sc[kb][j], l2, bias, dmv[kb][j]);
+        dsv[j] = bwd_prob<SM>(a, sc[j], l2, bias, dmv[j]);
       }
-    if (!full) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      if (!full) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int ko = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
           const int kd = kDoc ? Dk[buf][ko] : 0;
-          dsv[kb][j] = n0 + ko < a.Skv && bwd_visible<MK>(a, q, n0 + ko, qdoc, kd) ? dsv[kb][j] : 0.f;
+          dsv[j] = n0 + ko < a.Skv && bwd_visible<MK>(a, q, n0 + ko, qdoc, kd) ? dsv[j] : 0.f;
         }
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      }
+      bf16x8 dhi[2];
+      float dsmax = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float ds = dsv[kb][j] * (dp[kb][j] - dl) * dmv[kb][j];
-        dsv[kb][j] = ds;
+        const float ds = dsv[j] * (dp[j] - dl) * dmv[j];
+        dsv[j] = ds;
         dsmax = fmaxf(dsmax, fabsf(ds));
-        dhi[kb * 2 + (j >> 3)][j & 7] = (bf16)ds;
+        dhi[j >> 3][j & 7] = (bf16)ds;
       }
-    // dQ^T += K^T dS^T with dS rounded to bf16, plus its rounding residue
-    // (the lo half) where the tile holds a large |dS|: the row of dS sums
-    // to zero, so the products cancel (the threshold as in dK, dV)
-#pragma unroll
-    for (int d2 = 0; d2 < NDB; ++d2)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dqT[d2] = mfma32(vt_operand<D>(Ks[buf], t, d2 * 32, tl), dhi[t], dqT[d2]);
-    if (any_lane(dsmax > kLoThresh)) {
-      bf16x8 dlo[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          dlo[kb * 2 + (j >> 3)][j & 7] = (bf16)(dsv[kb][j] - (float)dhi[kb * 2 + (j >> 3)][j & 7]);
+      // dQ^T += K^T dS^T over these 32 keys (k-steps 2 kb, 2 kb + 1) with dS
+      // rounded to bf16, plus its rounding residue (the lo half) where the
+      // block holds a large |dS|: the row of dS sums to zero, so the products
+      // cancel (the threshold as in dK, dV)
 #pragma unroll
       for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) dqT[d2] = mfma32(vt_operand<D>(Ks[buf], t, d2 * 32, tl), dlo[t], dqT[d2]);
+        for (int tt = 0; tt < 2; ++tt)
+          dqT[d2] = mfma32(vt_operand<D>(Ks[buf], 2 * kb + tt, d2 * 32, tl), dhi[tt], dqT[d2]);
+      if (any_lane(dsmax > kLoThresh)) {
+        bf16x8 dlo[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dlo[j >> 3][j & 7] = (bf16)(dsv[j] - (float)dhi[j >> 3][j & 7]);
+#pragma unroll
+        for (int d2 = 0; d2 < NDB; ++d2)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+            dqT[d2] = mfma32(vt_operand<D>(Ks[buf], 2 * kb + tt, d2 * 32, tl), dlo[tt], dqT[d2]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
