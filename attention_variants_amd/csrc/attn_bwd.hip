@@ -93,13 +93,13 @@ __device__ __forceinline__ bool bwd_tile_full(const BwdArgs& a, int n0, int n1, 
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 128 keys of one (b, KV head); wave w owns keys
 // k0 + 32 w .. +31, held in registers as the B operand of S = Q K^T and
-// dP = dO V^T (lane = key).  Query tiles of 64 rows (two 32-row blocks) of
+// dP = dO V^T (lane = key).  Query tiles of 128 rows (four 32-row blocks) of
 // every query head of the group are staged in LDS, row-major and swizzled,
 // and read two ways: rows for the A operand of S and dP, transposed for the
 // A operand of dV^T += dO^T P and dK^T += Q^T dS.
 template <int SM, int MK>
 __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
-  constexpr int BQ = 64;
+  constexpr int BQ = 128;
   constexpr int QCH = BQ * CPR / NT;  // 16-byte chunks per thread per tensor
   constexpr bool kDoc = MK == MK_DOC;
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][BQ * D];
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
     const float slope2 =
         SM == SM_ALIBI ? uniform_f(kLog2e * exp2f(-a.alibi_max_bias * (float)(hq + 1) / (float)a.Hq)) : 0.f;
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
+    for (int blk = 0; blk < BQ / 32; ++blk) {
       const int qb0 = qt * BQ + 32 * blk;  // first query of the block
       const int qblast = qb0 + 31;
       // skip the block when no key of the wave is visible to any of its queries
