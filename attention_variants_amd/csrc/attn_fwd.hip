@@ -511,7 +511,10 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
             if constexpr (MK == MK_WINDOW) {
               ok = ok && (off > wlo);
             } else if constexpr (MK == MK_DOC) {
-              ok = ok && (Ds[buf][off + 4 * hh] == dq[qb]);
+              // the document ids of this lane's four keys (one 16-byte LDS
+              // read), and no short circuit: a branch and a read per score otherwise
+              const i32x4 d4 = *(const i32x4*)&Ds[buf][kb * 32 + 8 * (j >> 2) + 4 * hh];
+              ok = ok & (d4[j & 3] == dq[qb]);
             }
             s[qb][kb][j] = ok ? s[qb][kb][j] : neg_inf();
             if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bounds the live compare masks
