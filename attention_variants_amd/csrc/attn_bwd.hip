@@ -71,10 +71,18 @@ __device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, f
 template <int MK>
 __device__ __forceinline__ bool bwd_visible(const BwdArgs& a, int q, int kp, int qd, int kd) {
   if constexpr (MK == MK_CAUSAL) return kp <= q;
-  if constexpr (MK == MK_WINDOW) return kp <= q && q - kp < a.window;
-  if constexpr (MK == MK_PREFIX) return kp < a.prefix || kp <= q;
+  // (no short circuit: the callers' element loops stay free of branches)
+  if constexpr (MK == MK_WINDOW) return (kp <= q) & (q - kp < a.window);
+  if constexpr (MK == MK_PREFIX) return (kp < a.prefix) | (kp <= q);
   if constexpr (MK == MK_DOC) return qd == kd;
   return true;
+}
+
+// p where `ok`, else 0, with p computed on every lane first: a plain select
+// lets the compiler move p's exponential into a branch per element.
+__device__ __forceinline__ float keep_if(bool ok, float p) {
+  asm volatile("" : "+v"(p));
+  return ok ? p : 0.f;
 }
 
 // Whether every key n0..n1 of a tile is visible to every query qw..qwlast of
@@ -272,11 +280,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
       if (!full) {
+        i32x4 qd4[4];  // document ids of the block's query rows, four per 16-byte LDS read
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) qd4[g4] = kDoc ? *(const i32x4*)&Dq[buf][32 * blk + 8 * g4 + 4 * hh] : i32x4{};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int r = 8 * (j >> 2) + 4 * hh + (j & 3);
-          const int qd = kDoc ? Dq[buf][32 * blk + r] : 0;
-          pv[j] = bwd_visible<MK>(a, qb0 + r, key, qd, kdoc) ? pv[j] : 0.f;
+          pv[j] = keep_if(bwd_visible<MK>(a, qb0 + r, key, qd4[j >> 2][j & 3], kdoc), pv[j]);
         }
       }
 #pragma unroll
@@ -511,6 +521,9 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
       }
       // the element mask only on tiles that are not full (two copies of the
       // accumulation, so that full tiles carry no mask registers)
+      i32x4 kd4[4];  // document ids of this lane's keys, four per 16-byte LDS read
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) kd4[g4] = kDoc ? *(const i32x4*)&Dk[buf][kb * 32 + 8 * g4 + 4 * hh] : i32x4{};
       auto accumulate = [&](auto masked) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -521,8 +534,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
             float dmod;
             float p = bwd_prob<SM>(a, sc[qb][j], l2[qb], bias, dmod);
             if constexpr (decltype(masked)::value) {
-              const int kd = kDoc ? Dk[buf][ko] : 0;
-              p = n0 + ko < a.Skv && bwd_visible<MK>(a, qi[qb], n0 + ko, qdoc[qb], kd) ? p : 0.f;
+              p = keep_if((n0 + ko < a.Skv) & bwd_visible<MK>(a, qi[qb], n0 + ko, qdoc[qb], kd4[j >> 2][j & 3]), p);
             }
             psum[qb] += p;
             pdsum[qb] = fmaf(p, dp[qb][j], pdsum[qb]);
@@ -704,11 +716,13 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
         dsv[j] = bwd_prob<SM>(a, sc[j], l2, bias, dmv[j]);
       }
       if (!full) {
+        i32x4 kd4[4];  // document ids of this lane's keys, four per 16-byte LDS read
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) kd4[g4] = kDoc ? *(const i32x4*)&Dk[buf][kb * 32 + 8 * g4 + 4 * hh] : i32x4{};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int ko = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          const int kd = kDoc ? Dk[buf][ko] : 0;
-          dsv[j] = n0 + ko < a.Skv && bwd_visible<MK>(a, q, n0 + ko, qdoc, kd) ? dsv[j] : 0.f;
+          dsv[j] = keep_if((n0 + ko < a.Skv) & bwd_visible<MK>(a, q, n0 + ko, qdoc, kd4[j >> 2][j & 3]), dsv[j]);
         }
       }
       bf16x8 dhi[2];
