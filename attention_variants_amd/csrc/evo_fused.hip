@@ -33,6 +33,8 @@
 // residue blocks per wave, whose m operand stays in registers through both
 // projection phases (see evo_fused_fits for the measured limit).
 
+#include <type_traits>
+
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"
 
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   __shared__ __attribute__((aligned(16))) bf16 Vs[LMAX * DH];
   __shared__ __attribute__((aligned(16))) bf16 Us[C::U_ELEMS];  // W slice (phases A, B), bias slots (C)
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so the per-wave guards are scalar
   const int hh = lane >> 5, l32 = lane & 31;
   const int total = a.Ns * a.H;
   const int L = xcd_remap(blockIdx.x, total);
@@ -124,24 +127,29 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   // Stage the head's slice of two projections, [Wa | Wb] = [FCM x 2 DH],
   // row-major and swizzled for transposed reads.
   auto stage_w = [&](const void* wa, const void* wb) {
-    constexpr int CH = FCM * WW / 8;  // 16-byte chunks
+    // one pass per matrix: a per-lane choice between the two buffer
+    // descriptors would make the descriptor divergent (a loop per load)
+    constexpr int CH = FCM * DH / 8;  // 16-byte chunks of one matrix's slice
     static_assert(CH % NT == 0, "W slice / thread mismatch");
     const auto ars = make_rsrc(wa, (uint32_t)FCM * HD * 2);
     const auto brs = make_rsrc(wb, (uint32_t)FCM * HD * 2);
-    i32x4 t[CH / NT];
+    i32x4 t[2][CH / NT];
 #pragma unroll
-    for (int c = 0; c < CH / NT; ++c) {
-      const int idx = tid + NT * c;
-      const int row = idx / (WW / 8), col = (idx % (WW / 8)) * 8;
-      const uint32_t off = (uint32_t)(row * HD + h * DH + (col % DH)) * 2;
-      t[c] = col < DH ? buf_load16(ars, off) : buf_load16(brs, off);
-    }
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int c = 0; c < CH / NT; ++c) {
-      const int idx = tid + NT * c;
-      const int row = idx / (WW / 8), col = (idx % (WW / 8)) * 8;
-      *(i32x4*)&Us[tr_tile_off<WW>(row, col)] = t[c];
-    }
+      for (int c = 0; c < CH / NT; ++c) {
+        const int idx = tid + NT * c;
+        const int row = idx / (DH / 8), col = (idx % (DH / 8)) * 8;
+        t[m][c] = buf_load16(m == 0 ? ars : brs, (uint32_t)(row * HD + h * DH + col) * 2);
+      }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int c = 0; c < CH / NT; ++c) {
+        const int idx = tid + NT * c;
+        const int row = idx / (DH / 8), col = (idx % (DH / 8)) * 8;
+        *(i32x4*)&Us[tr_tile_off<WW>(row, m * DH + col)] = t[m][c];
+      }
   };
 
   // The m operand of every k-step of this wave's residue blocks, loaded once
@@ -162,15 +170,23 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int i = 0; i < MT; ++i) acc[cb][i] = f32x16{};
+    auto run = [&](auto all) {
 #pragma unroll
-    for (int t = 0; t < NST; ++t) {
+      for (int t = 0; t < NST; ++t) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const bf16x8 wf = w_operand(t, 32 * cb);
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x8 wf = w_operand(t, 32 * cb);
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
-          if (i < nmine) acc[cb][i] = mfma32(wf, mall[i][t], acc[cb][i]);
+          for (int i = 0; i < MT; ++i)
+            if (decltype(all)::value || i < nmine) acc[cb][i] = mfma32(wf, mall[i][t], acc[cb][i]);
+        }
       }
+    };
+    // the usual case (every wave owns MT blocks) without a branch per MFMA
+    if (nmine == MT) {
+      run(std::true_type{});
+    } else {
+      run(std::false_type{});
     }
   };
 
