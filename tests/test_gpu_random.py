@@ -1,13 +1,15 @@
-"""Seeded random parity sweep of the forward, backward and decode entry points
-against the fp64 oracle, through the C ABI.
+"""Seeded random parity sweep against the fp64 oracle, through the C ABI: the
+forward, the backward, dense and paged decode, differential attention and the
+two Evoformer forms.
 
-Each case draws its own shape and parameters (head dimension, batch, query and
-KV heads, ragged and cross lengths, score modifier, mask, softmax scale,
-softcap, ALiBi maximum bias, bias-tensor broadcast, window, prefix and document
-lengths, page size and per-sequence cache lengths) from a fixed generator, so
-the sweep is the same on every run and a failure names its case.
-Every output row is compared. Gates as in the fixed-shape tests:
-|gpu - oracle| <= 1e-2 + 1e-2 |oracle|; LSE within 1e-3 + 1e-5 relative.
+Each case draws its own shape and parameters from a fixed generator: head
+dimension, batch, query and KV heads, ragged and cross lengths, score modifier,
+mask, softmax scale, softcap, ALiBi maximum bias, bias-tensor broadcast, window,
+prefix and document lengths, page size and per-sequence cache lengths, lambda,
+MSA channels, heads and residues.  The sweep is the same on every run and a
+failure names its case.  Every output row is compared.  Gates as in the
+fixed-shape tests: |gpu - oracle| <= 1e-2 + 1e-2 |oracle|; LSE within 1e-3 +
+1e-5 relative.
 """
 
 import numpy as np
@@ -266,3 +268,101 @@ def test_paged_decode_random(gpu_lib, case):
                                                  page_size=ps, score_mod=score_mod, mask=mask, **okw)
     assert_close(out.float().cpu().numpy(), ref, what)
     assert_close(lse.cpu().numpy(), ref_lse, what + " lse", atol=1e-3, rtol=1e-5)
+
+
+def _diff_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 7))
+        S = int(rng.integers(1, 400))
+        Dh, Dv = [(64, 128), (64, 64), (32, 64), (32, 128)][int(rng.integers(0, 4))]
+        lam = float(np.round(rng.uniform(-0.5, 1.5), 3))
+        causal = bool(rng.random() < 0.7)
+        scale = float(rng.choice([0.0, 0.5 / np.sqrt(Dh)]))
+        cases.append((i, B, H, S, Dh, Dv, lam, causal, scale))
+    return cases
+
+
+DIFF_CASES = _diff_cases(24, 20261207)
+
+
+@pytest.mark.parametrize("case", DIFF_CASES,
+                         ids=[f"{c[0]}-B{c[1]}-H{c[2]}-S{c[3]}-Dh{c[4]}-Dv{c[5]}" for c in DIFF_CASES])
+def test_diff_random(gpu_lib, case):
+    i, B, H, S, Dh, Dv, lam, causal, scale = case
+    x = wi.diff_inputs(B, H, S, Dh, Dv, seeds=(1900 + i, 2000 + i, 2100 + i))
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    what = f"diff B{B} H{H} S{S} Dh{Dh} Dv{Dv} lam{lam} causal{causal} scale{scale}"
+    print(what, flush=True)
+    out, big = canary_empty((B, H, S, Dv), torch.bfloat16)
+    gpu_lib.diff_attn_fwd(q, k, v, lam=lam, scale=scale, causal=causal, out=out)
+    torch.cuda.synchronize()
+    assert canary_intact(big, out.numel()), "write past the end of out: " + what
+    ref = oracle.diff_attention(f64(x["q"]), f64(x["k"]), f64(x["v"]), lam=lam, causal=causal,
+                                scale=None if scale == 0.0 else scale)
+    assert_close(out.float().cpu().numpy(), ref, what)
+
+
+def _evo_cases(n, seed, fused_share, ns_range):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dh = int(rng.choice([32, 64]))
+        H = int(rng.choice([4, 8, 12, 16] if dh == 32 else [2, 4, 6, 8]))
+        if rng.random() < fused_share:  # the one-launch row-wise form: Cm 256, N_res <= 256, a multiple of 8
+            Cm, Nr = 256, 8 * int(rng.integers(1, 33))
+        else:
+            Cm, Nr = int(rng.choice([64, 128, 256, 320])), int(rng.integers(1, 300))
+        Ns = int(rng.integers(*ns_range))
+        cases.append((i, Ns, Nr, Cm, H, dh))
+    return cases
+
+
+EVO_CASES = _evo_cases(24, 20261208, 0.5, (1, 10))
+# Column-wise attention runs over the Ns sequences of a residue column.  With
+# only a few of them the bf16 rounding of the projected q and k (the MFMA
+# operands) alone moves the output past the gate where it nearly cancels: exact
+# fp64 attention over bf16-rounded projections reaches 0.96, 1.16 and 1.06 of
+# the gate at Ns = 2, 6 and 8 (Nr 240-267, Cm 64-128).  The pages' shape has
+# Ns = 128; the sweep draws Ns from 16 up.
+EVO_COL_CASES = _evo_cases(16, 20261209, 0.0, (16, 49))
+
+
+def _evo_inputs(i, Ns, Nr, Cm, H, dh):
+    return wi.evoformer_inputs(Ns, Nr, Cm, H, dh, seeds={"m": 2200 + i, "wq": 2300 + i, "wk": 2400 + i,
+                                                         "wv": 2500 + i, "wg": 2600 + i, "bias": 2700 + i})
+
+
+@pytest.mark.parametrize("case", EVO_CASES, ids=[f"{c[0]}-Ns{c[1]}-Nr{c[2]}-Cm{c[3]}-H{c[4]}x{c[5]}" for c in EVO_CASES])
+def test_evoformer_row_random(gpu_lib, case):
+    i, Ns, Nr, Cm, H, dh = case
+    x = _evo_inputs(i, Ns, Nr, Cm, H, dh)
+    t = {n: to_dev(x[n]) for n in x}
+    what = f"evoformer row Ns{Ns} Nr{Nr} Cm{Cm} H{H} dh{dh}"
+    print(what, flush=True)
+    out, big = canary_empty((Ns, Nr, H * dh), torch.bfloat16)
+    gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=H, dh=dh, out=out)
+    torch.cuda.synchronize()
+    assert canary_intact(big, out.numel()), "write past the end of out: " + what
+    ref = oracle.evoformer_row_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]), f64(x["wg"]),
+                                               f64(x["bias"]), H=H, dh=dh)
+    assert_close(out.float().cpu().numpy(), ref, what)
+
+
+@pytest.mark.parametrize("case", EVO_COL_CASES,
+                         ids=[f"{c[0]}-Ns{c[1]}-Nr{c[2]}-Cm{c[3]}-H{c[4]}x{c[5]}" for c in EVO_COL_CASES])
+def test_evoformer_col_random(gpu_lib, case):
+    i, Ns, Nr, Cm, H, dh = case
+    x = _evo_inputs(100 + i, Ns, Nr, Cm, H, dh)
+    t = {n: to_dev(x[n]) for n in x}
+    what = f"evoformer col Ns{Ns} Nr{Nr} Cm{Cm} H{H} dh{dh}"
+    print(what, flush=True)
+    out, big = canary_empty((Ns, Nr, H * dh), torch.bfloat16)
+    gpu_lib.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], H=H, dh=dh, out=out)
+    torch.cuda.synchronize()
+    assert canary_intact(big, out.numel()), "write past the end of out: " + what
+    ref = oracle.evoformer_col_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]), f64(x["wg"]),
+                                               H=H, dh=dh)
+    assert_close(out.float().cpu().numpy(), ref, what)
