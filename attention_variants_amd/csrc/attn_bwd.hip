@@ -49,6 +49,46 @@ constexpr int CPR = D / 8;    // 16-byte chunks per row
 // the pairs exist for) always takes the pair.
 constexpr float kLoThresh = 0.125f;
 
+// LDS tiles that the gradient kernels read both ways: as 16-byte row pieces
+// (the A operand of S and dP) and transposed (the operand of dV^T, dK^T, dQ^T).
+// Rows are 128 bytes (D = 64), half of the 256-byte bank window.  A row read
+// serves 16 lanes per pass from 16 consecutive rows, so those 16 pieces need
+// 16 distinct 16-byte slots; a transposed read serves 32 lanes from 4
+// consecutive rows, whose 64-byte pieces need 4 distinct 64-byte segments.
+// The 16-byte chunks of row r are XOR-swizzled by pi((r >> 1) mod 8) with
+// pi(m) = 4 (m mod 2) + m / 2: a permutation (row reads conflict-free), and
+// the two same-parity rows of every aligned group of 4 rows get different
+// 64-byte halves (transposed reads conflict-free).  A swizzle of whole 64-byte
+// segments serves only the transposed reads and costs the row reads four
+// passes each.
+static_assert(D == 64, "the dual-read swizzle is laid out for 128-byte rows");
+__device__ __forceinline__ int dual_swz(int row) {
+  const int m = (row >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
+// Element offset of the 8-element chunk starting at column c (c % 8 == 0).
+__device__ __forceinline__ int dual_off(int row, int c) { return row * D + (c ^ (dual_swz(row) << 3)); }
+
+// Per-lane parts of a transposed read of a dual tile: rows base + row0 and
+// base + row0 + 8 (base a multiple of 16), columns dcol + col0 .. + 3; the two
+// rows take different chunk swizzles, both per-lane constants.
+struct DualLane {
+  int row0, col0, xlo, xhi;
+  __device__ __forceinline__ explicit DualLane(int lane)
+      : row0(4 * (lane >> 5) + ((lane & 15) >> 2)),
+        col0(16 * ((lane >> 4) & 1) + 4 * (lane & 3)),
+        xlo(dual_swz(4 * (lane >> 5) + ((lane & 15) >> 2)) << 3),
+        xhi(dual_swz(4 * (lane >> 5) + ((lane & 15) >> 2) + 8) << 3) {}
+};
+
+// Transposed operand (32 columns from dcol x 16 rows) of k-step t of a dual tile.
+__device__ __forceinline__ bf16x8 dual_vt_operand(const bf16* tile, int t, int dcol, const DualLane& dl) {
+  const bf16* rp = tile + ((t >> 1) * 32 + 16 * (t & 1) + dl.row0) * D;
+  const i16x4 lo = lds_read_tr16(rp + ((dcol + dl.col0) ^ dl.xlo));
+  const i16x4 hi = lds_read_tr16(rp + 8 * D + ((dcol + dl.col0) ^ dl.xhi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Score pieces shared by both gradient kernels, for one element: raw q.k in
 // `s`, query position qp, key position kp.  Returns p = exp(t - lse) (0 when
 // masked) and writes the factor mod'(scale q.k) to `dmod`.
@@ -146,7 +186,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
   f32x16 dkT[NDB], dvT[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dkT[db] = dvT[db] = f32x16{};
-  const TrLane<D> tl(lane);
+  const DualLane tl(lane);
   const bool key_live = key < a.Skv;
   const int* docrow = kDoc ? a.doc + (size_t)b * a.Skv : nullptr;
   const int kdoc = kDoc ? docrow[min(key, a.Skv - 1)] : 0;
@@ -206,8 +246,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < QCH; ++c) {
       const int idx = tid + NT * c;
-      *(i32x4*)&Qs[buf][tr_tile_off<D>(idx / CPR, (idx % CPR) * 8)] = qr[c];
-      *(i32x4*)&Gs[buf][tr_tile_off<D>(idx / CPR, (idx % CPR) * 8)] = gr[c];
+      *(i32x4*)&Qs[buf][dual_off(idx / CPR, (idx % CPR) * 8)] = qr[c];
+      *(i32x4*)&Gs[buf][dual_off(idx / CPR, (idx % CPR) * 8)] = gr[c];
     }
     if (tid < BQ) {
       Ls[buf][tid] = lr;
@@ -261,7 +301,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
       f32x16 sc = {}, dp = {};
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
-        const int off = tr_tile_off<D>(32 * blk + l32, s * 16 + hh * 8);
+        const int off = dual_off(32 * blk + l32, s * 16 + hh * 8);
         sc = mfma32(*(const bf16x8*)&Qs[buf][off], kreg[s], sc);
         dp = mfma32(*(const bf16x8*)&Gs[buf][off], vreg[s], dp);
       }
@@ -310,8 +350,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
       for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-          dvT[d2] = mfma32(vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl), phi[tt], dvT[d2]);
-          dkT[d2] = mfma32(vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl), dhi[tt], dkT[d2]);
+          dvT[d2] = mfma32(dual_vt_operand(Gs[buf], 2 * blk + tt, d2 * 32, tl), phi[tt], dvT[d2]);
+          dkT[d2] = mfma32(dual_vt_operand(Qs[buf], 2 * blk + tt, d2 * 32, tl), dhi[tt], dkT[d2]);
         }
       // ... plus their rounding residues (the bf16 lo halves) where the block
       // holds a large value: where attention concentrates, the sums over
@@ -327,7 +367,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
         for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-            dvT[d2] = mfma32(vt_operand<D>(Gs[buf], 2 * blk + tt, d2 * 32, tl), plo[tt], dvT[d2]);
+            dvT[d2] = mfma32(dual_vt_operand(Gs[buf], 2 * blk + tt, d2 * 32, tl), plo[tt], dvT[d2]);
       }
       if (lo_ds) {
         bf16x8 dlo[2];
@@ -337,7 +377,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
         for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-            dkT[d2] = mfma32(vt_operand<D>(Qs[buf], 2 * blk + tt, d2 * 32, tl), dlo[tt], dkT[d2]);
+            dkT[d2] = mfma32(dual_vt_operand(Qs[buf], 2 * blk + tt, d2 * 32, tl), dlo[tt], dkT[d2]);
       }
     }
   }
@@ -620,7 +660,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
   f32x16 dqT[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqT[db] = f32x16{};
-  const TrLane<D> tl(lane);
+  const DualLane tl(lane);
 
   // the forward's analytic key range of the query tile [q0, qlast]
   const int nKV = (a.Skv + BN - 1) / BN;
@@ -667,7 +707,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int idx = tid + NT * c;
-      const int off = tr_tile_off<D>(idx / CPR, (idx % CPR) * 8);
+      const int off = dual_off(idx / CPR, (idx % CPR) * 8);
       *(i32x4*)&Ks[buf][off] = kr[c];
       *(i32x4*)&Vs[buf][off] = vr[c];
     }
@@ -704,7 +744,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
       f32x16 sc = {}, dp = {};
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
-        const int off = tr_tile_off<D>(kb * 32 + l32, s * 16 + hh * 8);
+        const int off = dual_off(kb * 32 + l32, s * 16 + hh * 8);
         sc = mfma32(*(const bf16x8*)&Ks[buf][off], qreg[s], sc);
         dp = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp);
       }
@@ -742,7 +782,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
       for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-          dqT[d2] = mfma32(vt_operand<D>(Ks[buf], 2 * kb + tt, d2 * 32, tl), dhi[tt], dqT[d2]);
+          dqT[d2] = mfma32(dual_vt_operand(Ks[buf], 2 * kb + tt, d2 * 32, tl), dhi[tt], dqT[d2]);
       if (any_lane(dsmax > kLoThresh)) {
         bf16x8 dlo[2];
 #pragma unroll
@@ -751,7 +791,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
         for (int d2 = 0; d2 < NDB; ++d2)
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt)
-            dqT[d2] = mfma32(vt_operand<D>(Ks[buf], 2 * kb + tt, d2 * 32, tl), dlo[tt], dqT[d2]);
+            dqT[d2] = mfma32(dual_vt_operand(Ks[buf], 2 * kb + tt, d2 * 32, tl), dlo[tt], dqT[d2]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
