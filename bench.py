@@ -570,6 +570,48 @@ def run_profile(what, steps, nres=256):
         torch.cuda.synchronize()
         print(json.dumps({"profile": what, "B": B, "H": H, "S": S, "D": D, "window": 256, "launches": steps}))
         return
+    if what == "kernels":
+        # one launch family after another, `steps` launches each, for counters
+        # that compare the instantiations (16k tokens: B = 4, S = 4096): the
+        # forward at D = 32 and 128 with softcap under four masks (GQA 16/2,
+        # document mask in natural order), the bias tensor, ALiBi causal and
+        # PrefixLM at D = 64, both differential shapes, the column-wise
+        # Evoformer at N_res 256 and dense decode (64 x 4096 keys)
+        B, S = 4, 4096
+        for D in (32, 128):
+            x = wi.attention_inputs(B, 16, 2, S, S, D)
+            q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+            for mk in ("none", "causal", "sliding_window", "document"):
+                kw = dict(mask=mk, score_mod="softcap")
+                if mk == "document":
+                    kw["doc_id"] = torch.from_numpy(wi.doc_ids(4, B, S)).to(dev)
+                for _ in range(steps):
+                    av.attn_fwd(q, k, v, **kw)
+        x = wi.attention_inputs(B, 16, 16, S, S, 64)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        bias = _dev(wi.normal_bf16(18, (1, 16, S, S), 2.0), dev)
+        for _ in range(steps):
+            av.attn_fwd(q, k, v, score_mod="bias", bias=bias)
+        del bias
+        for mk in ("causal", "prefix_lm"):
+            for _ in range(steps):
+                av.attn_fwd(q, k, v, mask=mk, score_mod="alibi", prefix_len=S // 4)
+        for Dh, Dv, H in ((64, 128, 16), (32, 64, 32)):
+            x = wi.diff_inputs(B, H, S, Dh, Dv)
+            q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+            for _ in range(steps):
+                av.diff_attn_fwd(q, k, v)
+        x = wi.evoformer_inputs(128, 256, 256, 8, 32)
+        t = {n: _dev(x[n], dev) for n in x}
+        for _ in range(steps):
+            av.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], H=8, dh=32)
+        x = wi.attention_inputs(64, 32, 8, 1, 4096, 64)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        for _ in range(steps):
+            av.attn_decode_fwd(q, k, v, score_mod="softcap", mask="causal")
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "kernels", "launches_each": steps}))
+        return
     if what == "diff":
         x = wi.diff_inputs(4, 16, 4096)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -603,7 +645,7 @@ def main():
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
                                           "document", "window", "causal",
-                                          "decode", "decode_b1", "bwd", "bias"],
+                                          "decode", "decode_b1", "bwd", "bias", "kernels"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
