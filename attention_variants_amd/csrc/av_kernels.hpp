@@ -183,8 +183,8 @@ struct EvoArgs {
 };
 size_t evo_workspace_bytes(int Ns, int Nr, int H, int dh);
 hipError_t launch_evoformer(const EvoArgs& a, hipStream_t stream);
-// The row-wise form in one launch (projections kept on chip, no workspace
-// traffic) for the shapes whose K and V fit one workgroup's LDS.
+// Both forms in one launch (projections kept on chip, no workspace traffic)
+// for the shapes whose K and V fit one workgroup's LDS.
 bool evo_fused_fits(const EvoArgs& a);
 hipError_t launch_evo_fused(const EvoArgs& a, hipStream_t stream);
 

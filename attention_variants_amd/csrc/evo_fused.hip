@@ -1,15 +1,20 @@
-// Evoformer row-wise gated self-attention with pair bias in one kernel, gfx950.
+// Evoformer gated self-attention in one kernel, gfx950: row-wise with pair
+// bias, and column-wise (no bias).
 //
 // The operation is the one evoformer.hip computes in two launches (talk
 // notes "Flashlight: PyTorch Compiler Extensions to Accelerate Attention
 // Variants", "Evaluation: complex attention variants"; reading: per MSA
 // sequence s and head h, q, k, v, g = m Wq, m Wk, m Wv, m Wg and
-// out[s, i, h*dh + e] = sigmoid(g_i[e]) * softmax_j(scale q_i.k_j + bias[h, i, j]) v_j[e]).
+// out[s, i, h*dh + e] = sigmoid(g_i[e]) * softmax_j(scale q_i.k_j + bias[h, i, j]) v_j[e];
+// column-wise the same over the sequences of one residue column, without
+// the bias).  The text below says "residues" for the tokens of one
+// attention problem; column-wise they are the sequences of the column.
 // Here the projections never leave the chip, as the pages' fusion does for
 // this variant (talk notes, "Compiler design" 3: the intermediate is not
 // written to global memory):
 //
-//  * One workgroup = one (sequence, head).  Its NW waves own the 32-residue
+//  * One workgroup = one (sequence, head), column-wise one (residue column,
+//    head).  Its NW waves own the 32-residue
 //    blocks w, w + NW, ... of the sequence.
 //  * Phase A: K and V of every residue, C^T = W^T m^T with the head's
 //    [Wk | Wv] slice staged in LDS (read transposed as the MFMA A operand)
@@ -25,13 +30,14 @@
 //    barrier in the key loop.  The pair bias of a 32 x 64 tile is loaded as
 //    coalesced 16-byte row chunks into a wave-private LDS slot, one tile
 //    ahead, and read back as the initial value of the QK^T accumulators.
-//  * Sequences outermost in the grid, heads innermost, remapped so that one
-//    XCD runs the heads of a few sequences side by side: each m row comes
-//    from HBM once and then from that XCD's L2.
-// Instantiated for Cm = 256, dh in {32, 64} and up to 256 residues (N_res a
-// multiple of 8): K and V of the whole sequence in LDS and at most two
-// residue blocks per wave, whose m operand stays in registers through both
-// projection phases (see evo_fused_fits for the measured limit).
+//  * Sequences (columns) outermost in the grid, heads innermost, remapped so
+//    that one XCD runs the heads of a few sequences side by side: each m row
+//    comes from HBM once and then from that XCD's L2.
+// Instantiated for Cm = 256, dh in {32, 64} and up to 256 residues (row-wise
+// N_res a multiple of 8, for the 16-byte bias rows): K and V of the whole
+// sequence in LDS and at most two residue blocks per wave, whose m operand
+// stays in registers through both projection phases (see evo_fused_fits for
+// the measured limit).
 
 #include <type_traits>
 
@@ -55,15 +61,21 @@ __device__ __forceinline__ int k_chunk(int row, int c) {
   return row * DH + 8 * (c ^ ((row / RPW) % CPR));
 }
 
-template <int DH, int NW, int LMAX>
+// WS: the W slice of a projection phase is staged in WS parts of FCM / WS
+// rows (channels of m), the next part's loads in flight during the current
+// part's MFMAs.
+template <int DH, int NW, int LMAX, int WS>
 struct FusedCfg {
   static constexpr int NT = NW * 64;
   static constexpr int MT = (LMAX / 32 + NW - 1) / NW;    // 32-residue blocks per wave
   static constexpr int NCB = 2 * DH / 32;                 // 32-channel blocks of one projection pair
-  static constexpr int W_ELEMS = FCM * 2 * DH;            // [Wk | Wv] or [Wq | Wg] slice
+  static constexpr int W_ELEMS = FCM / WS * 2 * DH;       // one part of the [Wk | Wv] or [Wq | Wg] slice
   static constexpr int SLOT_ELEMS = 32 * FBP;             // one wave's bias slot
   static constexpr int U_ELEMS = W_ELEMS > NW * SLOT_ELEMS ? W_ELEMS : NW * SLOT_ELEMS;
   static constexpr int LDS_BYTES = (2 * LMAX * DH + U_ELEMS) * 2;
+  // waves per SIMD the registers are sized for: three where the LDS holds
+  // three four-wave workgroups per CU (160 KB), else two
+  static constexpr int OCC = NW == 4 && 3 * LDS_BYTES <= 160 * 1024 ? 3 : 2;
 };
 
 // LDS-only workgroup barrier (the global stores of earlier phases need not
@@ -74,11 +86,11 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Two waves per SIMD either way: four-wave workgroups two per CU, eight-wave
-// workgroups one per CU.
-template <int DH, int NW, int LMAX>
-__global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs a) {
-  using C = FusedCfg<DH, NW, LMAX>;
+// Two waves per SIMD (four-wave workgroups two per CU, eight-wave workgroups
+// one per CU), three for the small-LDS four-wave forms.
+template <int DH, int NW, int LMAX, int WS, bool COL>
+__global__ __launch_bounds__(NW * 64, (FusedCfg<DH, NW, LMAX, WS>::OCC)) void evo_fused_row_kernel(const EvoArgs a) {
+  using C = FusedCfg<DH, NW, LMAX, WS>;
   constexpr int NT = C::NT, MT = C::MT, NCB = C::NCB;
   constexpr int NDB = DH / 32;   // d-blocks of O^T
   constexpr int NDS = DH / 16;   // QK^T k-steps
@@ -92,23 +104,27 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so the per-wave guards are scalar
   const int hh = lane >> 5, l32 = lane & 31;
-  const int total = a.Ns * a.H;
+  // The workgroup's attention runs over Nr tokens: row-wise the residues of
+  // sequence `s` (m rows s * Nr .. + Nr - 1), column-wise the sequences of
+  // residue column `s` (m rows s, s + Nr, ...; no pair bias).
+  const int total = (COL ? a.Nr : a.Ns) * a.H;
   const int L = xcd_remap(blockIdx.x, total);
   const int s = L / a.H, h = L % a.H;
-  const int Nr = a.Nr, HD = a.H * DH;
+  const int Nr = COL ? a.Ns : a.Nr, HD = a.H * DH;
+  const size_t tok_stride = COL ? (size_t)a.Nr * FCM : (size_t)FCM;  // elements between the tokens' m rows
   const int nTB = (Nr + 31) / 32;
   const int nKT = (Nr + FBN - 1) / FBN;  // 64-key tiles of the attention
-  // this wave's residue blocks: w, w + NW, ...
+  // this wave's token blocks: w, w + NW, ...
   const int nmine = w < nTB ? (nTB - 1 - w) / NW + 1 : 0;
 
-  // m rows of this sequence; rows past Nr read as zero (buffer bounds)
-  const uint32_t m_bytes = (uint32_t)Nr * FCM * 2;
-  const auto mrs = make_rsrc((const bf16*)a.m + (size_t)s * Nr * FCM, m_bytes);
+  // m rows of these tokens; rows past Nr read as zero (buffer bounds)
+  const uint32_t m_bytes = (uint32_t)(((size_t)(Nr - 1) * tok_stride + FCM) * 2);
+  const auto mrs = make_rsrc((const bf16*)a.m + (COL ? (size_t)s * FCM : (size_t)s * Nr * FCM), m_bytes);
   uint32_t mrow[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     const int r = (w + NW * i) * 32 + l32;
-    mrow[i] = (i < nmine && r < Nr) ? (uint32_t)r * FCM * 2 + hh * 16 : m_bytes;
+    mrow[i] = (i < nmine && r < Nr) ? (uint32_t)((size_t)r * tok_stride * 2) + hh * 16 : m_bytes;
   }
   // W^T operand of projection k-step t (32 channels from dcol x 16 rows of
   // m's channels): lane (channel l32, half hh) needs rows 16 t + 8 hh + 0..7,
@@ -124,24 +140,28 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // Stage the head's slice of two projections, [Wa | Wb] = [FCM x 2 DH],
-  // row-major and swizzled for transposed reads.
-  auto stage_w = [&](const void* wa, const void* wb) {
+  // The head's slice of two projections, [Wa | Wb] = [FCM x 2 DH], in WS
+  // parts of FCM / WS rows: load_w brings part `part` into registers,
+  // store_w writes it to LDS row-major, swizzled for transposed reads.
+  constexpr int WR = FCM / WS;      // rows of one part
+  constexpr int CH = WR * DH / 8;   // 16-byte chunks of one matrix's part
+  static_assert(CH % NT == 0, "W slice / thread mismatch");
+  using WRegs = i32x4[2][CH / NT];
+  auto load_w = [&](const void* wa, const void* wb, int part, WRegs& t) {
     // one pass per matrix: a per-lane choice between the two buffer
     // descriptors would make the descriptor divergent (a loop per load)
-    constexpr int CH = FCM * DH / 8;  // 16-byte chunks of one matrix's slice
-    static_assert(CH % NT == 0, "W slice / thread mismatch");
     const auto ars = make_rsrc(wa, (uint32_t)FCM * HD * 2);
     const auto brs = make_rsrc(wb, (uint32_t)FCM * HD * 2);
-    i32x4 t[2][CH / NT];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int c = 0; c < CH / NT; ++c) {
         const int idx = tid + NT * c;
-        const int row = idx / (DH / 8), col = (idx % (DH / 8)) * 8;
+        const int row = part * WR + idx / (DH / 8), col = (idx % (DH / 8)) * 8;
         t[m][c] = buf_load16(m == 0 ? ars : brs, (uint32_t)(row * HD + h * DH + col) * 2);
       }
+  };
+  auto store_w = [&](const WRegs& t) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -165,20 +185,18 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
 
   // C^T = [Wa | Wb]^T m^T for this wave's residue blocks: acc[cb][i] is the
   // 32 x 32 tile of channel block cb (cb < NCB / 2: Wa) and residue block i.
-  auto project = [&](f32x16 (&acc)[NCB][MT]) {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < MT; ++i) acc[cb][i] = f32x16{};
+  // The W part in LDS covers the k-steps part * NST / WS ..
+  auto project_part = [&](f32x16 (&acc)[NCB][MT], auto part) {
+    constexpr int T0 = decltype(part)::value * (NST / WS);
     auto run = [&](auto all) {
 #pragma unroll
-      for (int t = 0; t < NST; ++t) {
+      for (int t = 0; t < NST / WS; ++t) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const bf16x8 wf = w_operand(t, 32 * cb);
 #pragma unroll
           for (int i = 0; i < MT; ++i)
-            if (decltype(all)::value || i < nmine) acc[cb][i] = mfma32(wf, mall[i][t], acc[cb][i]);
+            if (decltype(all)::value || i < nmine) acc[cb][i] = mfma32(wf, mall[i][T0 + t], acc[cb][i]);
         }
       }
     };
@@ -189,13 +207,32 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
       run(std::false_type{});
     }
   };
+  // One projection phase: stage part 0 (the loads of part 1 go out behind
+  // it), project, and with two parts stage and project the second.
+  auto project = [&](const void* wa, const void* wb, f32x16 (&acc)[NCB][MT]) {
+    static_assert(WS == 1 || WS == 2, "one or two W parts");
+    WRegs wt;
+    load_w(wa, wb, 0, wt);
+    store_w(wt);
+    if constexpr (WS == 2) load_w(wa, wb, 1, wt);
+    lds_sync();
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < MT; ++i) acc[cb][i] = f32x16{};
+    project_part(acc, std::integral_constant<int, 0>{});
+    if constexpr (WS == 2) {
+      lds_sync();  // every wave is done with part 0
+      store_w(wt);
+      lds_sync();
+      project_part(acc, std::integral_constant<int, 1>{});
+    }
+  };
 
   // ---- phase A: K and V of every residue into LDS
-  stage_w(a.w[1], a.w[2]);
-  lds_sync();
   {
     f32x16 acc[NCB][MT];
-    project(acc);
+    project(a.w[1], a.w[2], acc);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       if (i >= nmine) continue;
@@ -232,13 +269,11 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   lds_sync();  // K, V complete; the W slice bytes are free
 
   // ---- phase B: q (scaled) and the gate of this wave's residues, in registers
-  stage_w(a.w[0], a.w[3]);
-  lds_sync();
   bf16x8 qreg[MT][NDS];
   bf16x4 gate[MT][NDB * 4];
   {
     f32x16 acc[NCB][MT];
-    project(acc);
+    project(a.w[0], a.w[3], acc);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -259,7 +294,7 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   // The pair-bias tiles of the wave's (block, key tile) sequence stream through
   // two register buffers, two tiles ahead, across block boundaries.
   bf16* slot = Us + w * C::SLOT_ELEMS;
-  const auto brs = make_rsrc((const bf16*)a.bias + (size_t)h * Nr * Nr, (uint32_t)Nr * Nr * 2);
+  const auto brs = make_rsrc(COL ? nullptr : (const bf16*)a.bias + (size_t)h * Nr * Nr, COL ? 0u : (uint32_t)Nr * Nr * 2);
   const TrLane<DH> vl(lane);
   const int nflat = nmine * nKT;
   // bias rows q0 .. q0+31, keys n0 .. n0+63 of flat tile f: lane loads row
@@ -273,12 +308,14 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
       dst[c] = buf_load16(brs, (uint32_t)((q0 + (lane >> 3) + 8 * c) * Nr + n0 + 8 * (lane & 7)) * 2);
   };
   i32x4 br0[4], br1[4];
-  if (nflat > 0) bload(0, br0);
-  if (nflat > 1) bload(1, br1);
+  if constexpr (!COL) {
+    if (nflat > 0) bload(0, br0);
+    if (nflat > 1) bload(1, br1);
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     if (i >= nmine) break;
-    if (i > 0 && (nKT & 1)) {  // the flat tile parity flips at this block
+    if (!COL && i > 0 && (nKT & 1)) {  // the flat tile parity flips at this block
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const i32x4 t = br0[c];
@@ -293,27 +330,33 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
     RowState st;
     auto step = [&](int kt, i32x4 (&bcur)[4]) {
       const int n0 = kt * FBN;
-      // stage this tile's bias (wave-private slot; the wave's LDS accesses
-      // execute in order, so no barrier), then fetch the tile two ahead
+      if constexpr (!COL) {
+        // stage this tile's bias (wave-private slot; the wave's LDS accesses
+        // execute in order, so no barrier), then fetch the tile two ahead
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bf16* dst = slot + ((lane >> 3) + 8 * c) * FBP + 8 * (lane & 7);
-        *(i32x2*)dst = i32x2{bcur[c][0], bcur[c][1]};
-        *(i32x2*)(dst + 4) = i32x2{bcur[c][2], bcur[c][3]};
+        for (int c = 0; c < 4; ++c) {
+          bf16* dst = slot + ((lane >> 3) + 8 * c) * FBP + 8 * (lane & 7);
+          *(i32x2*)dst = i32x2{bcur[c][0], bcur[c][1]};
+          *(i32x2*)(dst + 4) = i32x2{bcur[c][2], bcur[c][3]};
+        }
+        const int f = i * nKT + kt;
+        if (f + 2 < nflat) bload(f + 2, bcur);
       }
-      const int f = i * nKT + kt;
-      if (f + 2 < nflat) bload(f + 2, bcur);
-      // S^T = K Q^T + bias: the accumulators start at the bias
+      // S^T = K Q^T (+ bias: row-wise the accumulators start at the bias)
       f32x16 sc[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
+        if constexpr (COL) {
+          sc[kb] = f32x16{};
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const i32x2 b2 = *(const i32x2*)(slot + l32 * FBP + 32 * kb + 8 * g + 4 * hh);
+          for (int g = 0; g < 4; ++g) {
+            const i32x2 b2 = *(const i32x2*)(slot + l32 * FBP + 32 * kb + 8 * g + 4 * hh);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int wd = b2[e >> 1];
-            sc[kb][4 * g + e] = __builtin_bit_cast(float, (e & 1) ? (wd & (int)0xffff0000) : (wd << 16));
+            for (int e = 0; e < 4; ++e) {
+              const int wd = b2[e >> 1];
+              sc[kb][4 * g + e] = __builtin_bit_cast(float, (e & 1) ? (wd & (int)0xffff0000) : (wd << 16));
+            }
           }
         }
         const int key = n0 + 32 * kb + l32;
@@ -354,12 +397,14 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
       step(kt, br0);
       if (kt + 1 < nKT) step(kt + 1, br1);
     }
-    // epilogue: out[s, q, h*DH + d] = sigmoid(g) * O / l
+    // epilogue: out[token, h*DH + d] = sigmoid(g) * O / l (token (s, q)
+    // row-wise, (q, s) column-wise)
     const int q = q0 + l32;
     const float l_tot = xhalf_sum(st.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (q < Nr) {
-      bf16* orow = (bf16*)a.out + ((size_t)s * Nr + q) * HD + (size_t)h * DH;
+      const size_t tok = COL ? (size_t)q * a.Nr + s : (size_t)s * Nr + q;
+      bf16* orow = (bf16*)a.out + tok * HD + (size_t)h * DH;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -377,26 +422,45 @@ __global__ __launch_bounds__(NW * 64, 2) void evo_fused_row_kernel(const EvoArgs
   }
 }
 
-template <int DH, int NW, int LMAX>
+template <int DH, int NW, int LMAX, int WS, bool COL>
 hipError_t launch_fused(const EvoArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((evo_fused_row_kernel<DH, NW, LMAX>), dim3(a.Ns * a.H), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((evo_fused_row_kernel<DH, NW, LMAX, WS, COL>), dim3((COL ? a.Nr : a.Ns) * a.H), dim3(NW * 64),
+                     0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Up to 256 residues: same-box timings at 128 sequences, against the two
-// launches, 52.7 vs 58.6 us (8 x 32) and 43.3 vs 56.4 us (4 x 64).  At 384
-// residues (eight waves, one workgroup per CU) the single launch measured
-// 96.9 against 91.1 us: its serial phases no longer overlap another
-// workgroup's, so longer sequences keep the two launches.
+// Row-wise, up to 256 residues: same-box timings at 128 sequences, against
+// the two launches, 52.7 vs 58.6 us (8 x 32) and 43.3 vs 56.4 us (4 x 64).
+// At 384 residues (eight waves, one workgroup per CU) the single launch
+// measured 96.9 against 91.1 us: its serial phases no longer overlap another
+// workgroup's, so longer sequences keep the two launches.  Column-wise over
+// 128 sequences (the 128-token forms), against the two launches at 256 / 384
+// / 768 residues: 36.8 / 51.7 / 94.0 vs 52.7 / 68.0 / 138.0 us (8 x 32) and
+// 32.7 / 45.7 / 84.6 vs 51.4 / 67.0 / 137.0 us (4 x 64; with the W slice in
+// one part, 96 KB of LDS and one workgroup per CU, 45.3 / 65.8 / 126.5 us).
+// Over 256 sequences (the 256-token forms) at 256 residues: 75.9 vs 94.6 us
+// (8 x 32) and 77.7 vs 93.8 us (4 x 64).
 bool evo_fused_fits(const EvoArgs& a) {
-  return !a.col && a.Cm == FCM && a.Nr % 8 == 0 && a.Nr <= 256 && (a.dh == 32 || a.dh == 64);
+  if (a.Cm != FCM || (a.dh != 32 && a.dh != 64)) return false;
+  if (a.col) return a.Ns <= 256 && (size_t)a.Ns * a.Nr * FCM * 2 < (1ull << 31);
+  return a.Nr % 8 == 0 && a.Nr <= 256;
 }
 
 hipError_t launch_evo_fused(const EvoArgs& a, hipStream_t stream) {
-  if (a.dh == 64) return launch_fused<64, 8, 256>(a, stream);
-  return launch_fused<32, 4, 256>(a, stream);
+  if (a.col) {
+    // four waves and the LDS of 128 tokens: 48 KB at dh 32 (three workgroups
+    // per CU), 64 KB at dh 64 with the W slice in two parts (two per CU)
+    if (a.Ns <= 128) {
+      if (a.dh == 64) return launch_fused<64, 4, 128, 2, true>(a, stream);
+      return launch_fused<32, 4, 128, 1, true>(a, stream);
+    }
+    if (a.dh == 64) return launch_fused<64, 8, 256, 1, true>(a, stream);
+    return launch_fused<32, 4, 256, 1, true>(a, stream);
+  }
+  if (a.dh == 64) return launch_fused<64, 8, 256, 1, false>(a, stream);
+  return launch_fused<32, 4, 256, 1, false>(a, stream);
 }
 
 }  // namespace av

@@ -24,9 +24,11 @@
 //     fastest within a head so bias[h] stays resident in L2.
 //
 // The column-wise form (attention over the sequences of each residue column,
-// no pair bias) runs the same two launches: the GEMM orders tokens column-
-// major and writes planes [Nr, H, Ns, dh], and the attention kernel takes one
-// (residue, head) per problem with the gated epilogue only.
+// no pair bias) runs the same two launches where it does not take the
+// one-kernel path (more than 256 sequences, or Cm other than 256): the GEMM
+// orders tokens column-major and writes planes [Nr, H, Ns, dh], and the
+// attention kernel takes one (residue, head) per problem with the gated
+// epilogue only.
 
 #include "attn_tile.hpp"
 #include "av_kernels.hpp"

@@ -295,7 +295,9 @@ int evoformer_gated_attn_fwd(const void* m, const void* wq, const void* wk, cons
  *   m    [Ns, Nr, Cm]      w* [Cm, H*dh] each      (no pair bias)
  *   out  [Ns, Nr, H*dh]
  * Workspace, scale, supported shapes and errors as evoformer_gated_attn_fwd;
- * the workspace size is the same (evoformer_workspace_bytes). */
+ * the workspace size is the same (evoformer_workspace_bytes).  With Cm = 256
+ * and Ns <= 256, one kernel keeps the projections on chip and leaves the
+ * workspace untouched (it is still required). */
 int evoformer_col_gated_attn_fwd(const void* m, const void* wq, const void* wk, const void* wv, const void* wg,
                                  void* out, void* workspace, size_t workspace_bytes, int Ns, int Nr, int Cm, int H,
                                  int dh, float scale, hipStream_t stream);

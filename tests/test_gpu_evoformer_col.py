@@ -96,6 +96,14 @@ def test_head_width_64(gpu_lib, Ns):
     _run(gpu_lib, Ns, 5, Cm=256, H=4, dh=64)
 
 
+@pytest.mark.parametrize("dh", [32, 64])
+@pytest.mark.parametrize("Ns", [127, 128, 129, 255, 256, 257, 300])
+def test_sequence_counts_at_the_kernel_limits(gpu_lib, Ns, dh):
+    """Cm 256 on both sides of each limit: the one-kernel path over 128 tokens
+    and over 256 tokens, then the two launches past 256 sequences."""
+    _run(gpu_lib, Ns, 3, Cm=256, H=8 if dh == 32 else 4, dh=dh)
+
+
 @pytest.mark.parametrize("Nr", [256, 768])
 def test_benchmark_shapes_4x64(gpu_lib, Nr):
     rng = np.random.default_rng(9)
