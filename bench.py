@@ -459,7 +459,7 @@ def run_sweep(path, steps, warmup):
     f.close()
 
 
-def run_profile(what, steps, nres=256):
+def run_profile(what, steps, nres=256, evo_heads=8):
     """Launch one kernel `steps` times with nothing else on the stream."""
     import torch
 
@@ -478,7 +478,7 @@ def run_profile(what, steps, nres=256):
 
     av.load_library()
     if what == "evoformer":
-        Ns, Nr, Cm, Hh, dh = 128, nres, 256, 8, 32
+        Ns, Nr, Cm, Hh, dh = 128, nres, 256, evo_heads, 256 // evo_heads
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
         t = {n: _dev(x[n], dev) for n in x}
         ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
@@ -488,10 +488,10 @@ def run_profile(what, steps, nres=256):
             av.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=Hh, dh=dh,
                                         workspace=ws, out=out)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": "evoformer", "Ns": Ns, "Nr": Nr, "launches": steps}))
+        print(json.dumps({"profile": "evoformer", "Ns": Ns, "Nr": Nr, "H": Hh, "dh": dh, "launches": steps}))
         return
     if what == "evoformer_col":
-        Ns, Nr, Cm, Hh, dh = 128, nres, 256, 8, 32
+        Ns, Nr, Cm, Hh, dh = 128, nres, 256, evo_heads, 256 // evo_heads
         x = wi.evoformer_inputs(Ns, Nr, Cm, Hh, dh)
         t = {n: _dev(x[n], dev) for n in x}
         ws = torch.empty(av.evoformer_workspace_bytes(Ns, Nr, Hh, dh), dtype=torch.uint8, device=dev)
@@ -501,7 +501,7 @@ def run_profile(what, steps, nres=256):
             av.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], H=Hh, dh=dh,
                                             workspace=ws, out=out)
         torch.cuda.synchronize()
-        print(json.dumps({"profile": "evoformer_col", "Ns": Ns, "Nr": Nr, "launches": steps}))
+        print(json.dumps({"profile": "evoformer_col", "Ns": Ns, "Nr": Nr, "H": Hh, "dh": dh, "launches": steps}))
         return
     if what in ("decode", "decode_b1"):
         B, Hq, Hkv, Skv, D = (64, 32, 8, 4096, 64) if what == "decode" else (1, 32, 8, 16384, 64)
@@ -642,6 +642,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--nres", type=int, default=256, help="N_res of the Evoformer profile run")
+    ap.add_argument("--evo-heads", type=int, default=8, choices=[8, 4],
+                    help="heads of the Evoformer profile run: 8 x 32 or 4 x 64")
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
                                           "document", "window", "causal",
@@ -658,7 +660,7 @@ def main():
         run_sweep(args.sweep, args.steps, args.warmup)
         return
     if args.profile:
-        run_profile(args.profile, args.steps, args.nres)
+        run_profile(args.profile, args.steps, args.nres, args.evo_heads)
         return
     # the CPU baseline runs first: its pool forks a process that has not touched the GPU
     cpu_rec = None if args.no_cpu_baseline else cpu_baseline(args.cpu_budget)
