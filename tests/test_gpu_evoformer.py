@@ -157,3 +157,23 @@ def test_fused_form_deterministic(gpu_lib):
     r = [gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=8, dh=32)
          for _ in range(3)]
     assert torch.equal(r[0], r[1]) and torch.equal(r[1], r[2])
+
+
+@pytest.mark.parametrize("Nr, Cm, one_launch", [(256, 256, True), (200, 256, True), (260, 256, False),
+                                                (256, 128, False)])
+def test_workspace_use_follows_the_path(gpu_lib, Nr, Cm, one_launch):
+    """Cm 256 with N_res <= 256 (a multiple of 8) keeps the projections on
+    chip and leaves the workspace bytes alone; the two-launch path writes its
+    planes."""
+    Ns, H, dh = 2, 8, 32
+    x = wi.evoformer_inputs(Ns, Nr, Cm, H, dh)
+    t = {n: to_dev(x[n]) for n in x}
+    ws = torch.full((gpu_lib.evoformer_workspace_bytes(Ns, Nr, H, dh),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = gpu_lib.evoformer_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], t["bias"], H=H, dh=dh,
+                                           workspace=ws)
+    torch.cuda.synchronize()
+    untouched = bool((ws == 0xA5).all().item())
+    assert untouched == one_launch
+    ref = oracle.evoformer_row_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]), f64(x["wg"]),
+                                               f64(x["bias"]), H=H, dh=dh)
+    assert_close(out.float().cpu().numpy(), ref, f"evoformer row Nr{Nr} Cm{Cm}")

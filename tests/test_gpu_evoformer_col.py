@@ -110,3 +110,21 @@ def test_benchmark_shapes_4x64(gpu_lib, Nr):
     seqs = np.unique(np.concatenate([[0, 1, 63, 64, 127], rng.integers(0, 128, 12)]))
     cols = np.unique(np.concatenate([[0, 1, Nr - 1, Nr // 2], rng.integers(0, Nr, 28)]))
     _run(gpu_lib, 128, Nr, H=4, dh=64, seqs=seqs, cols=cols)
+
+
+@pytest.mark.parametrize("Ns, Cm, one_launch", [(128, 256, True), (256, 256, True), (257, 256, False),
+                                                (128, 128, False)])
+def test_workspace_use_follows_the_path(gpu_lib, Ns, Cm, one_launch):
+    """Cm 256 with at most 256 sequences keeps the projections on chip and
+    leaves the workspace bytes alone; the two-launch path writes its planes."""
+    Nr, H, dh = 5, 4, 64
+    x = wi.evoformer_inputs(Ns, Nr, Cm, H, dh)
+    t = {n: to_dev(x[n]) for n in ("m", "wq", "wk", "wv", "wg")}
+    ws = torch.full((gpu_lib.evoformer_workspace_bytes(Ns, Nr, H, dh),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = gpu_lib.evoformer_col_gated_attn_fwd(t["m"], t["wq"], t["wk"], t["wv"], t["wg"], H=H, dh=dh, workspace=ws)
+    torch.cuda.synchronize()
+    untouched = bool((ws == 0xA5).all().item())
+    assert untouched == one_launch
+    ref = oracle.evoformer_col_gated_attention(f64(x["m"]), f64(x["wq"]), f64(x["wk"]), f64(x["wv"]),
+                                               f64(x["wg"]), H=H, dh=dh)
+    assert_close(out.float().cpu().numpy(), ref, f"evoformer col Ns{Ns} Cm{Cm}")
