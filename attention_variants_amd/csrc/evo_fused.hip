@@ -14,11 +14,12 @@
 // written to global memory):
 //
 //  * One workgroup = one (sequence, head), column-wise one (residue column,
-//    head).  Its NW waves own the 32-residue
-//    blocks w, w + NW, ... of the sequence.
+//    head).  Its NW waves own the 32-residue blocks w, w + NW, ... of the
+//    sequence.
 //  * Phase A: K and V of every residue, C^T = W^T m^T with the head's
-//    [Wk | Wv] slice staged in LDS (read transposed as the MFMA A operand)
-//    and the m rows loaded straight from memory as the B operand; the
+//    [Wk | Wv] slice staged in LDS (read transposed as the MFMA A operand;
+//    in two halves of the channels where LDS is short, see FusedCfg) and
+//    the m rows loaded straight from memory as the B operand; the
 //    results go to LDS, K with its columns in the order the QK^T operands
 //    want (so no register shuffle is needed), V swizzled for transposed reads.
 //  * Phase B: q (softmax scale folded in before the one bf16 rounding) and
@@ -27,9 +28,10 @@
 //    layout of S^T = K Q^T, g in the layout of the O^T accumulator.
 //  * Phase C: each wave runs the fused attention of its 32-row blocks over
 //    all residues with K and V resident in LDS, so the waves never meet: no
-//    barrier in the key loop.  The pair bias of a 32 x 64 tile is loaded as
-//    coalesced 16-byte row chunks into a wave-private LDS slot, one tile
-//    ahead, and read back as the initial value of the QK^T accumulators.
+//    barrier in the key loop.  Row-wise, the pair bias of a 32 x 64 tile is
+//    loaded as coalesced 16-byte row chunks into a wave-private LDS slot,
+//    two tiles ahead, and read back as the initial value of the QK^T
+//    accumulators; column-wise the accumulators start at zero.
 //  * Sequences (columns) outermost in the grid, heads innermost, remapped so
 //    that one XCD runs the heads of a few sequences side by side: each m row
 //    comes from HBM once and then from that XCD's L2.
