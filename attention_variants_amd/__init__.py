@@ -426,10 +426,11 @@ def attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D) -> int:
 
 def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, softcap=20.0,
              alibi_max_bias=8.0, window=256, prefix_len=0, doc_id=None, kv_group=0, dq=None, dk=None, dv=None,
-             workspace=None):
+             workspace=None, doc_order=None):
     """Gradients (dq, dk, dv) of attn_fwd's output for an upstream ``dout``; ``lse``
     is attn_fwd's (``return_lse=True``).  Every mask of attn_fwd, with the same
-    ``window`` / ``prefix_len`` / ``doc_id``."""
+    ``window`` / ``prefix_len`` / ``doc_id``; ``doc_order`` (document mask only)
+    is the work order ``attn_doc_order(doc_id)`` returns, as for attn_fwd."""
     import torch
 
     lib = load_library()
@@ -458,12 +459,16 @@ def attn_bwd(q, k, v, dout, lse, *, score_mod="none", mask="none", scale=0.0, so
         _need_shape(dv, "dv", torch.bfloat16, (B, Hkv, Skv, D), dev)
     if doc_id is not None:
         _need_shape(doc_id, "doc_id", torch.int32, (B, Sq), dev)
+    if doc_order is not None:
+        _need(doc_order, "doc_order", torch.int32, 1, dev)
+        if doc_order.numel() != attn_doc_order_len(B, Sq):
+            raise ValueError("doc_order must come from attn_doc_order(doc_id) of this shape")
     need = lib.attn_bwd_workspace_bytes(B, Hq, Hkv, Sq, Skv, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     ws_bytes = _need_workspace(workspace, "workspace", need, dev)
     var = make_variant(score_mod, mask, scale=scale, softcap=softcap, alibi_max_bias=alibi_max_bias,
-                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group)
+                       window=window, prefix_len=prefix_len, doc_id=doc_id, kv_group=kv_group, doc_order=doc_order)
     rc = lib.attn_bwd(ctypes.byref(var), q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
                       ws_bytes, B, Hq, Hkv, Sq, Skv, D, _stream_ptr(dev))

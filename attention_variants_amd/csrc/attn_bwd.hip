@@ -38,6 +38,29 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int D = 64;
+
+// Workgroup -> (tile, b * heads + head) through the document work order of
+// attn_doc_order: entry blockIdx.x / heads is a (sequence, 128-row tile)
+// pair, heaviest first, and the heads of one pair are consecutive blocks
+// (with heads a multiple of 8 every XCD keeps the same heads throughout).
+// Under the document mask a 128-key tile spans the same documents as the
+// 128-row query tile at its position, so one order serves the key-owner
+// launch too.  False for an entry outside B * nT (not an order of this
+// shape): the workgroup then touches nothing.
+__device__ __forceinline__ bool ordered_tile(const int* order, int heads, int B, int nT, int& tile, int& bh) {
+  const int item = order[blockIdx.x / heads];
+  if (item < 0 || item >= B * nT) return false;
+  tile = item % nT;
+  bh = (item / nT) * heads + blockIdx.x % heads;
+  return true;
+}
+
+// Query rows per statistics workgroup: two 32-row blocks per wave, one under
+// the document mask (the forward's tile there, and the tile of its order)
+template <int MK>
+constexpr int stats_bm() {
+  return MK == MK_DOC ? 128 : 256;
+}
 constexpr int NDS = D / 16;   // k-steps over the head dimension
 constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
 constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -164,6 +187,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
     const TileIdx ti = weighted_tile(blockIdx.x, a.total, nKT);
     kt = ti.mt_lin;
     bk = ti.bh;
+  } else if (MK == MK_DOC && a.doc_order != nullptr) {
+    if (!ordered_tile(a.doc_order, a.Hkv, a.B, nKT, kt, bk)) return;
   } else {
     const int L = xcd_remap(blockIdx.x, a.total);
     kt = L % nKT;
@@ -403,7 +428,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Row statistics (launch 1).  Workgroup = 256 query rows of one (b, query
-// head), wave = 64 rows as two 32-row blocks in the forward's layout:
+// head), wave = 64 rows as two 32-row blocks in the forward's layout (128
+// rows and one block per wave under the document mask, see stats_bm):
 // S^T = K Q^T and dP^T = V dO^T with Q and dO in registers (lane = query),
 // so each K and V fragment read from LDS feeds the MFMAs of both blocks.
 // K and V are only read as rows here, so both tiles use the forward's padded
@@ -412,8 +438,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 template <int SM, int MK>
 __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) {
   constexpr int BN = 64;
-  constexpr int QB = 2;
-  constexpr int BM = 4 * 32 * QB;
+  constexpr int BM = stats_bm<MK>();
+  constexpr int QB = BM / 128;
   constexpr int NCH = BN * CPR / NT;
   constexpr int KP = D + 8;
   constexpr bool kDoc = MK == MK_DOC;
@@ -430,6 +456,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
     const TileIdx ti = weighted_tile(blockIdx.x, gridDim.x, nM);
     mt_lin = ti.mt_lin;
     bh = ti.bh;
+  } else if (kDoc && a.doc_order != nullptr) {
+    if (!ordered_tile(a.doc_order, a.Hq, a.B, nM, mt_lin, bh)) return;
   } else {
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     mt_lin = L % nM;
@@ -624,6 +652,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
     const TileIdx ti = weighted_tile(blockIdx.x, a.total_q, nM);
     mt_lin = ti.mt_lin;
     bh = ti.bh;
+  } else if (kDoc && a.doc_order != nullptr) {
+    if (!ordered_tile(a.doc_order, a.Hq, a.B, nM, mt_lin, bh)) return;
   } else {
     const int L = xcd_remap(blockIdx.x, a.total_q);
     mt_lin = L % nM;
@@ -817,7 +847,8 @@ __global__ __launch_bounds__(NT) void zero_fill_kernel(i32x4* p, size_t n16) {
 
 template <int SM, int MK>
 hipError_t launch_bwd2(const BwdArgs& a, hipStream_t stream) {
-  const int total_s = a.B * a.Hq * ((a.Sq + 255) / 256);
+  constexpr int BMS = stats_bm<MK>();
+  const int total_s = a.B * a.Hq * ((a.Sq + BMS - 1) / BMS);
   hipLaunchKernelGGL((attn_bwd_stats_kernel<SM, MK>), dim3(total_s), dim3(NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -86,6 +86,18 @@ int attn_doc_order(const int32_t* doc_id, int B, int S, int32_t* order, int orde
   return hip_status(av::launch_doc_order(doc_id, B, S, order, stream));
 }
 
+// The document work order of av_variant, as attn_fwd and attn_bwd read it:
+// the kernels read entry blockIdx.x / heads < B * ceil(Sq / 128), so the
+// order must be the one attn_doc_order writes for this B and Sq.
+static int check_doc_order(const av_variant* var, int B, int Sq) {
+  if (var->doc_order == nullptr) return AV_OK;
+  if (var->mask != AV_MASK_DOCUMENT) return AV_ERR_PARAM;
+  if (!aligned(var->doc_order, 4)) return AV_ERR_ALIGN;
+  const int n = attn_doc_order_len(B, Sq);
+  if (n < 0) return n;
+  return var->doc_order_len == n ? AV_OK : AV_ERR_PARAM;
+}
+
 int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v, void* out, float* lse, int B,
              int Hq, int Hkv, int Sq, int Skv, int D, hipStream_t stream) {
   if (var == nullptr) return AV_ERR_NULL;
@@ -111,15 +123,7 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return AV_ERR_ALIGN;
   if (lse != nullptr && !aligned(lse, 4)) return AV_ERR_ALIGN;
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
-  if (var->doc_order != nullptr && var->mask != AV_MASK_DOCUMENT) return AV_ERR_PARAM;
-  if (var->doc_order != nullptr && !aligned(var->doc_order, 4)) return AV_ERR_ALIGN;
-  if (var->doc_order != nullptr) {
-    // the kernel reads entry blockIdx.x / Hq < B * ceil(Sq / 128): the order
-    // must be the one attn_doc_order writes for this B and Sq
-    const int n = attn_doc_order_len(B, Sq);
-    if (n < 0) return n;
-    if (var->doc_order_len != n) return AV_ERR_PARAM;
-  }
+  if (const int rc = check_doc_order(var, B, Sq); rc != AV_OK) return rc;
   // bias rows are read 8 bytes at a time when Skv % 4 == 0: every slice must
   // then start on an 8-byte boundary
   if (tbias && (!aligned(var->bias, 8) ||
@@ -383,6 +387,7 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
     return AV_ERR_ALIGN;
   if (var->mask == AV_MASK_DOCUMENT && !aligned(var->doc_id, 4)) return AV_ERR_ALIGN;
+  if (const int rc = check_doc_order(var, B, Sq); rc != AV_OK) return rc;
   if ((uint64_t)(Sq + 256) * D * 2 > kMaxSliceBytes || (uint64_t)(Skv + 128) * D * 2 > kMaxSliceBytes)
     return AV_ERR_TOO_LARGE;
   const int64_t total = (int64_t)B * Hkv * ((Skv + 127) / 128);
@@ -433,6 +438,7 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.window = var->window;
   a.prefix = var->prefix_len;
   a.doc = var->mask == AV_MASK_DOCUMENT ? var->doc_id : nullptr;
+  a.doc_order = var->mask == AV_MASK_DOCUMENT ? var->doc_order : nullptr;
   return hip_status(av::launch_attn_bwd(a, var->score_mod, var->mask, stream));
 }
 

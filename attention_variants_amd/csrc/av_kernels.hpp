@@ -142,6 +142,7 @@ struct BwdArgs {
   int window;         // MK_WINDOW
   int prefix;         // MK_PREFIX
   const int* doc;     // MK_DOC: [B, S] document ids
+  const int* doc_order;  // MK_DOC, optional: heaviest-first order of the 128-row tiles (attn_doc_order)
 };
 hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int mask, hipStream_t stream);
 // Zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel (no memset

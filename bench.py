@@ -376,8 +376,9 @@ def run_sweep(path, steps, warmup):
                   "frac_mfma_peak_visible": round(tf / PEAK_BF16_TFLOPS, 4)})
     # backward at the headline shape (algorithmic work: 5 products of 2*S*S*D
     # per head, i.e. 2.5x the forward's visible FLOPs)
-    for (sm, mk) in (("none", "none"), ("softcap", "causal"), ("none", "causal"), ("none", "sliding_window"),
-                     ("none", "prefix_lm"), ("none", "document")):
+    for (sm, mk_case) in (("none", "none"), ("softcap", "causal"), ("none", "causal"), ("none", "sliding_window"),
+                          ("none", "prefix_lm"), ("none", "document"), ("none", "document+order")):
+        mk = "document" if mk_case == "document+order" else mk_case
         B, H, S, D = 4, 16, 4096, 64
         x = wi.attention_inputs(B, H, H, S, S, D)
         q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
@@ -385,13 +386,16 @@ def run_sweep(path, steps, warmup):
         mkw = dict(window=256, prefix_len=S // 4,
                    doc_id=torch.from_numpy(wi.doc_ids(4, B, S)).to(dev) if mk == "document" else None)
         out, lse = av.attn_fwd(q, k, v, score_mod=sm, mask=mk, return_lse=True, **mkw)
+        if mk_case == "document+order":
+            # the forward's heaviest-first order, built once per document layout
+            mkw["doc_order"] = av.attn_doc_order(mkw["doc_id"])
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(av.attn_bwd_workspace_bytes(B, H, H, S, S, D), dtype=torch.uint8, device=dev)
         _, per = time_launches([lambda: av.attn_bwd(q, k, v, dout, lse, score_mod=sm, mask=mk, dq=dq, dk=dk, dv=dv,
                                                     workspace=ws, **mkw)], steps, warmup)
         fl = 2.5 * attn_flops(B, H, S, D, mk, window=256, prefix_len=S // 4, doc_lens=wi.doc_lengths(4, B, S))
         tf = fl / (per[0] * 1e-3) / 1e12
-        emit({"kernel": "attn_bwd", "score_mod": sm, "mask": mk, "B": B, "H": H, "S": S, "D": D,
+        emit({"kernel": "attn_bwd", "score_mod": sm, "mask": mk_case, "B": B, "H": H, "S": S, "D": D,
               "us": round(per[0] * 1e3, 2), "algorithmic_tflops": round(tf, 1),
               "frac_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
     # decoding: one new query per sequence against its key/value cache

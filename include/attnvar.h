@@ -100,11 +100,11 @@ typedef struct {
   int64_t bias_head_stride;
   /* AV_MASK_DOCUMENT, optional (NULL = natural order): device int32 order of
    * the query tiles written by attn_doc_order for the same doc_id, B and S.
-   * It changes only the order in which attn_fwd visits its work, never a
-   * result bit.  Non-NULL with any other mask is AV_ERR_PARAM; 4-byte
-   * aligned.  Read by attn_fwd only. */
+   * It changes only the order in which attn_fwd and attn_bwd visit their
+   * work, never a result bit.  Non-NULL with any other mask is
+   * AV_ERR_PARAM; 4-byte aligned.  Read by attn_fwd and attn_bwd. */
   const int32_t* doc_order;
-  /* Entries the doc_order buffer holds.  attn_fwd reads exactly
+  /* Entries the doc_order buffer holds.  attn_fwd and attn_bwd read exactly
    * n = attn_doc_order_len(B, Sq) of them; doc_order_len != n is
    * AV_ERR_PARAM (an order built for another shape), and a shape for which
    * attn_doc_order_len fails is that function's error.  Ignored when
@@ -142,7 +142,7 @@ int attn_fwd(const av_variant* variant, const void* q, const void* k, const void
  * for 128-row tile t of sequence b) sorted by the number of 64-key tiles
  * their documents span, largest first, ties by ascending index.  The order
  * depends only on doc_id: compute it once per document layout and pass it
- * as av_variant.doc_order to every attn_fwd call (layer, head count, score
+ * as av_variant.doc_order to every attn_fwd and attn_bwd call (layer, head count, score
  * modifier, D) over that layout.
  *   doc_id [B, S] int32 device, non-decreasing rows (as av_variant.doc_id)
  *   order  [order_len] int32 device, caller-owned, 4-byte aligned; the
@@ -224,6 +224,9 @@ int attn_decode_paged_fwd(const av_variant* variant, const void* q, const void* 
  * Supported: D = 64; every mask of attn_fwd with its parameters in the
  * variant (window, prefix_len, doc_id; a mask needs Sq == Skv); every score
  * modifier but AV_SCORE_BIAS.  Sq > 0 with Skv == 0 writes a zero dq.
+ * Under the document mask the variant's doc_order (as for attn_fwd) orders
+ * the three launches heaviest first: a 128-key tile there spans the same
+ * documents as the 128-row query tile at its position.
  * Deterministic (no atomics). */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Skv, int D);
 int attn_bwd(const av_variant* variant, const void* q, const void* k, const void* v, const void* dout,

@@ -302,6 +302,26 @@ def test_backward_rejections(lib):
     assert call(dq=0x80000 + 4) == -4
     assert call(lse=0x70000 + 2) == -4
 
+    # the document work order, as for attn_fwd: only with the document mask,
+    # 4-byte aligned, of attn_doc_order_len(B, Sq) entries
+    def call_v(var, B=2, S=256):
+        return lib.attn_bwd(ctypes.byref(var), P, P2, P3, P4, 0x70000, 0x80000, 0x90000, 0xA0000, 0x200000,
+                            1 << 30, B, 4, 2, S, S, 64, None)
+
+    v = av.make_variant(mask="causal")
+    v.doc_order, v.doc_order_len = 0x80000, 4
+    assert call_v(v) == -7
+    v = av.make_variant(mask="document")
+    v.doc_id = 0x90000
+    v.doc_order, v.doc_order_len = 0x80002, 4
+    assert call_v(v) == -4
+    v.doc_order = 0x80000
+    for n in (0, 3, 5, 1 << 20):
+        v.doc_order_len = n
+        assert call_v(v) == -7, n
+    v.doc_order_len = 2
+    assert call_v(v, B=1, S=257) == -7          # 3 tiles of 128 rows
+
 
 def test_evoformer_column_rejections(lib):
     def call(m=P, w=P2, out=P4, ws=0x100000, wsb=None, Ns=2, Nr=16, Cm=64, H=4, dh=32, scale=0.0):

@@ -124,3 +124,44 @@ def test_bwd_no_keys_gives_zero_dq(gpu_lib):
     torch.cuda.synchronize()
     assert torch.all(dq == 0).item()
     assert dk.numel() == 0 and dv.numel() == 0
+
+
+@pytest.mark.parametrize("score_mod", ["none", "alibi", "softcap"])
+@pytest.mark.parametrize("B, Hq, Hkv, S", [(2, 4, 2, 1000), (4, 16, 16, 4096), (1, 8, 8, 16384)])
+def test_bwd_document_order_changes_no_bit(gpu_lib, score_mod, B, Hq, Hkv, S):
+    """The heaviest-first work order of attn_doc_order reorders the three
+    backward launches only: dq, dk and dv equal the natural order's bit for
+    bit (each element keeps its one writer and its arithmetic)."""
+    D = 64
+    x = wi.attention_inputs(B, Hq, Hkv, S, S, D, seeds=(31, 32, 33))
+    g = wi.normal_bf16(34, (B, Hq, S, D), 1.0)
+    q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    doc = torch.from_numpy(wi.doc_ids(4, B, S)).cuda()
+    order = gpu_lib.attn_doc_order(doc)
+    kw = dict(score_mod=score_mod, mask="document", doc_id=doc, softcap=20.0)
+    out, lse = gpu_lib.attn_fwd(q, k, v, return_lse=True, **kw)
+    natural = gpu_lib.attn_bwd(q, k, v, dout, lse, **kw)
+    ordered = gpu_lib.attn_bwd(q, k, v, dout, lse, doc_order=order, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), natural, ordered):
+        assert torch.equal(a, b), f"{name} differs under the order ({score_mod}, B{B} S{S})"
+
+
+def test_bwd_document_order_parity(gpu_lib):
+    """The ordered backward against the oracle (GQA, several documents per
+    128-row tile and documents over several tiles)."""
+    B, Hq, Hkv, S, D = 2, 4, 2, 1000, 64
+    x = wi.attention_inputs(B, Hq, Hkv, S, S, D, seeds=(41, 42, 43))
+    g = wi.normal_bf16(44, (B, Hq, S, D), 1.0)
+    q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    doc_np = wi.doc_ids(4, B, S)
+    doc = torch.from_numpy(doc_np).cuda()
+    kw = dict(score_mod="softcap", mask="document", softcap=20.0)
+    out, lse = gpu_lib.attn_fwd(q, k, v, return_lse=True, doc_id=doc, **kw)
+    dq, dk, dv = gpu_lib.attn_bwd(q, k, v, dout, lse, doc_id=doc, doc_order=gpu_lib.attn_doc_order(doc), **kw)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g), doc_id=doc_np, **kw)
+    what = f"bwd softcap/document ordered B{B} Hq{Hq} Hkv{Hkv} S{S}"
+    assert_close(dq.float().cpu().numpy(), rq, what + " dq")
+    assert_close(dk.float().cpu().numpy(), rk, what + " dk")
+    assert_close(dv.float().cpu().numpy(), rv, what + " dv")
