@@ -55,11 +55,14 @@ __device__ __forceinline__ bool ordered_tile(const int* order, int heads, int B,
   return true;
 }
 
-// Query rows per statistics workgroup: two 32-row blocks per wave, one under
-// the document mask (the forward's tile there, and the tile of its order)
+// Query rows per statistics workgroup: two 32-row blocks per wave; one under
+// the document and sliding-window masks, whose short per-row key ranges
+// favour more, smaller workgroups (the forward's tile there, and under the
+// document mask the tile of its order).  Same box, S = 4096: sliding window
+// 199 -> 185 us; unmasked, causal and PrefixLM within 1 % either way.
 template <int MK>
 constexpr int stats_bm() {
-  return MK == MK_DOC ? 128 : 256;
+  return MK == MK_DOC || MK == MK_WINDOW ? 128 : 256;
 }
 constexpr int NDS = D / 16;   // k-steps over the head dimension
 constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
@@ -429,7 +432,8 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Row statistics (launch 1).  Workgroup = 256 query rows of one (b, query
 // head), wave = 64 rows as two 32-row blocks in the forward's layout (128
-// rows and one block per wave under the document mask, see stats_bm):
+// rows and one block per wave under the document and window masks, see
+// stats_bm):
 // S^T = K Q^T and dP^T = V dO^T with Q and dO in registers (lane = query),
 // so each K and V fragment read from LDS feeds the MFMAs of both blocks.
 // K and V are only read as rows here, so both tiles use the forward's padded
