@@ -533,6 +533,26 @@ def run_profile(what, steps, nres=256, evo_heads=8):
         torch.cuda.synchronize()
         print(json.dumps({"profile": "bwd", "B": B, "H": H, "S": S, "D": D, "launches": steps}))
         return
+    if what == "bwd_document":
+        # the document mask, natural order then the heaviest-first order
+        B, H, S, D = 4, 16, 4096, 64
+        x = wi.attention_inputs(B, H, H, S, S, D)
+        q, k, v = (_dev(x[n], dev) for n in ("q", "k", "v"))
+        dout = _dev(wi.normal_bf16(5, (B, H, S, D), 1.0), dev)
+        doc = torch.from_numpy(wi.doc_ids(4, B, S)).to(dev)
+        out, lse = av.attn_fwd(q, k, v, mask="document", doc_id=doc, return_lse=True)
+        order = av.attn_doc_order(doc)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(av.attn_bwd_workspace_bytes(B, H, H, S, S, D), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for o in (None, order):
+            for _ in range(steps):
+                av.attn_bwd(q, k, v, dout, lse, mask="document", doc_id=doc, doc_order=o, dq=dq, dk=dk, dv=dv,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile": "bwd_document", "B": B, "H": H, "S": S, "D": D,
+                          "launches": steps, "orders": ["natural", "heaviest-first"]}))
+        return
     if what == "bias":
         B, H, S, D = 4, 16, 4096, 64
         x = wi.attention_inputs(B, H, H, S, S, D)
@@ -651,7 +671,7 @@ def main():
     ap.add_argument("--sweep", default=None, help="write one JSON line per shape/variant to this file")
     ap.add_argument("--profile", choices=["none", "alibi", "softcap", "copy", "evoformer", "evoformer_col", "diff",
                                           "document", "window", "causal",
-                                          "decode", "decode_b1", "bwd", "bias", "kernels"],
+                                          "decode", "decode_b1", "bwd", "bwd_document", "bias", "kernels"],
                     default=None,
                     help="launch only this kernel --steps times (for counter collection); 'copy' is a "
                          "plain 1 GiB device copy used to calibrate the HBM byte counters")
