@@ -62,17 +62,18 @@ constexpr int NT = 256;  // threads per workgroup (4 waves)
 // with two query blocks per wave, D = 128 or a bias tile at D = 64 (the
 // prefetched bias of the bias tensor or the Evoformer pair bias does not fit
 // a third wave's budget), three otherwise.
-template <int D, int SM, int MK>
+template <int D, int SM, int MK, bool ONE>
 constexpr int min_waves() {
-  return attn_qb(D, SM, MK) == 2 || D == 128 || ((SM == SM_TBIAS || SM == SM_BIAS) && D == 64) ? 2 : 3;
+  return (attn_qb(D, SM, MK) == 2 && !ONE) || D == 128 || ((SM == SM_TBIAS || SM == SM_BIAS) && D == 64) ? 2 : 3;
 }
 
 // EXACT: the row sums add the fp32 exponentials (calls that ask for lse), else
 // their bf16 copies (see exp_pack_sum).
-template <int D, int SM, int MK, bool EXACT>
-__global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(const AttnArgs a) {
-  constexpr int QB = attn_qb(D, SM, MK);  // 32-row query blocks per wave
-  constexpr int BM = attn_bm(D, SM, MK);  // query rows per workgroup
+// ONE: one query block per wave where attn_qb picks two (attn_one_block).
+template <int D, int SM, int MK, bool EXACT, bool ONE>
+__global__ __launch_bounds__(NT, (min_waves<D, SM, MK, ONE>())) void attn_fwd_kernel(const AttnArgs a) {
+  constexpr int QB = ONE ? 1 : attn_qb(D, SM, MK);  // 32-row query blocks per wave
+  constexpr int BM = 4 * 32 * QB;                  // query rows per workgroup
   constexpr bool kBias = SM == SM_BIAS || SM == SM_TBIAS;  // a bias tile is read per KV tile
   constexpr int WQ = 32 * QB;        // query rows per wave
   constexpr int NKB = BN / 32;       // 32-key blocks per tile (S^T MFMA rows)
@@ -737,9 +738,9 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK>())) void attn_fwd_kernel(
   }
 }
 
-template <int D, int SM, int MK, bool EXACT = false>
+template <int D, int SM, int MK, bool EXACT = false, bool ONE = false>
 hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, SM, MK, EXACT>), dim3(a.total), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, SM, MK, EXACT, ONE>), dim3(a.total), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -747,9 +748,17 @@ template <int D, int SM, bool EXACT>
 hipError_t launch_mask_x(const AttnArgs& a, int mask, hipStream_t stream) {
   switch (mask) {
     case MK_NONE: return launch_one<D, SM, MK_NONE, EXACT>(a, stream);
-    case MK_CAUSAL: return launch_one<D, SM, MK_CAUSAL, EXACT>(a, stream);
+    case MK_CAUSAL:
+      if constexpr (attn_qb(D, SM, MK_CAUSAL) == 2) {
+        if (a.one_block) return launch_one<D, SM, MK_CAUSAL, EXACT, true>(a, stream);
+      }
+      return launch_one<D, SM, MK_CAUSAL, EXACT>(a, stream);
     case MK_WINDOW: return launch_one<D, SM, MK_WINDOW, EXACT>(a, stream);
-    case MK_PREFIX: return launch_one<D, SM, MK_PREFIX, EXACT>(a, stream);
+    case MK_PREFIX:
+      if constexpr (attn_qb(D, SM, MK_PREFIX) == 2) {
+        if (a.one_block) return launch_one<D, SM, MK_PREFIX, EXACT, true>(a, stream);
+      }
+      return launch_one<D, SM, MK_PREFIX, EXACT>(a, stream);
     case MK_DOC: return launch_one<D, SM, MK_DOC, EXACT>(a, stream);
   }
   return hipErrorInvalidValue;

@@ -135,7 +135,8 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   if ((uint64_t)(Skv + 64) * D * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
   if (tbias && (uint64_t)(Sq + av::kAttnBMMax) * (Skv + 64) * 2 > kMaxSliceBytes) return AV_ERR_TOO_LARGE;
   const int sm = tbias ? av::SM_TBIAS : var->score_mod;
-  const int bm = av::attn_bm(D, sm, var->mask);
+  const bool one_block = av::attn_one_block(D, sm, var->mask, Sq);
+  const int bm = one_block ? 128 : av::attn_bm(D, sm, var->mask);
   const int64_t nM = ((int64_t)Sq + bm - 1) / bm;
   const int64_t total = (int64_t)B * Hq * nM;
   if (total > INT32_MAX) return AV_ERR_TOO_LARGE;
@@ -157,6 +158,7 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.g = Hq / Hkv;
   a.nM = (int)nM;
   a.total = (int)total;
+  a.one_block = one_block;
   const double scale = var->scale > 0.f ? (double)var->scale : 1.0 / sqrt((double)D);
   a.scale = (float)scale;
   a.c = (float)(scale * kLog2e);
