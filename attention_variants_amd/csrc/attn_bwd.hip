@@ -118,9 +118,17 @@ __device__ __forceinline__ bf16x8 dual_vt_operand(const bf16* tile, int t, int d
 // Score pieces shared by both gradient kernels, for one element: raw q.k in
 // `s`, query position qp, key position kp.  Returns p = exp(t - lse) (0 when
 // masked) and writes the factor mod'(scale q.k) to `dmod`.
-template <int SM>
+// POLY (softcap, a tile inside the cubic's range, bwd_poly_tile): the
+// forward's cubic, t = s (p0 + p1 s^2) = cap2 tanh(k s), and mod' = 1 - (t /
+// cap2)^2 from it; one exponential per element instead of two and a rcp.
+template <int SM, bool POLY = false>
 __device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, float slope2, float& dmod) {
-  if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+  if constexpr ((SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) && POLY) {
+    const float t = s * fmaf(s * s, a.sc_poly[1], a.sc_poly[0]);
+    const float z = t * a.sc_inv_cap2;
+    dmod = fmaf(-z, z, 1.f);
+    return exp2_fast(t - l2);
+  } else if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
     // t = cap2 - 2 cap2 u, u = 1 / (1 + 2^(s sc_k)); mod' = 1 - tanh^2 = 4 u (1 - u)
     const float cap2 = a.softcap * kLog2e;
     const float u = rcp_fast(1.f + exp2_fast(s * a.sc_k));
@@ -129,6 +137,17 @@ __device__ __forceinline__ float bwd_prob(const BwdArgs& a, float s, float l2, f
   } else {
     dmod = 1.f;
     return exp2_fast(fmaf(s, a.c, slope2 - l2));
+  }
+}
+
+// Whether the softcap cubic serves the NB S fragments of a wave: every raw
+// score within |raw| <= sc_poly_lim (wave-uniform; NaN fails the test).
+template <int SM, int NB>
+__device__ __forceinline__ bool bwd_poly_tile(const BwdArgs& a, const f32x16* s) {
+  if constexpr (SM == SM_SOFTCAP || SM == SM_SOFTCAP_FIXED) {
+    return !any_lane(!(block_absmax<NB>(s) <= a.sc_poly_lim));
+  } else {
+    return false;
   }
 }
 
@@ -336,16 +355,23 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dkdv_kernel(const BwdArgs a) {
       float pv[16], dsv[16], dmv[16];
       bf16x8 phi[2], dhi[2];
       float pmax = 0.f, dsmax = 0.f;
+      auto probs = [&](auto poly) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 l4 = *(const f32x4*)&Ls[buf][32 * blk + 8 * g4 + 4 * hh];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 l4 = *(const f32x4*)&Ls[buf][32 * blk + 8 * g4 + 4 * hh];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = 4 * g4 + e;
-          const int q = qb0 + 8 * g4 + 4 * hh + e;
-          const float bias = SM == SM_ALIBI ? slope2 * (float)(key - q) : 0.f;
-          pv[j] = bwd_prob<SM>(a, sc[j], l4[e], bias, dmv[j]);
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * g4 + e;
+            const int q = qb0 + 8 * g4 + 4 * hh + e;
+            const float bias = SM == SM_ALIBI ? slope2 * (float)(key - q) : 0.f;
+            pv[j] = bwd_prob<SM, decltype(poly)::value>(a, sc[j], l4[e], bias, dmv[j]);
+          }
         }
+      };
+      if (bwd_poly_tile<SM, 1>(a, &sc)) {
+        probs(std::true_type{});
+      } else {
+        probs(std::false_type{});
       }
       if (!full) {
         i32x4 qd4[4];  // document ids of the block's query rows, four per 16-byte LDS read
@@ -596,7 +622,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
       i32x4 kd4[4];  // document ids of this lane's keys, four per 16-byte LDS read
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) kd4[g4] = kDoc ? *(const i32x4*)&Dk[buf][kb * 32 + 8 * g4 + 4 * hh] : i32x4{};
-      auto accumulate = [&](auto masked) {
+      auto accumulate = [&](auto masked, auto poly) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -604,7 +630,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
             const int ko = kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
             const float bias = SM == SM_ALIBI ? slope2 * (float)(n0 + ko - qi[qb]) : 0.f;
             float dmod;
-            float p = bwd_prob<SM>(a, sc[qb][j], l2[qb], bias, dmod);
+            float p = bwd_prob<SM, decltype(poly)::value>(a, sc[qb][j], l2[qb], bias, dmod);
             if constexpr (decltype(masked)::value) {
               p = keep_if((n0 + ko < a.Skv) & bwd_visible<MK>(a, qi[qb], n0 + ko, qdoc[qb], kd4[j >> 2][j & 3]), p);
             }
@@ -612,10 +638,19 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_stats_kernel(const BwdArgs a) 
             pdsum[qb] = fmaf(p, dp[qb][j], pdsum[qb]);
           }
       };
+      const bool poly = bwd_poly_tile<SM, QB>(a, sc);
       if (full) {
-        accumulate(std::false_type{});
+        if (poly) {
+          accumulate(std::false_type{}, std::true_type{});
+        } else {
+          accumulate(std::false_type{}, std::false_type{});
+        }
       } else {
-        accumulate(std::true_type{});
+        if (poly) {
+          accumulate(std::true_type{}, std::true_type{});
+        } else {
+          accumulate(std::true_type{}, std::false_type{});
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // one 32-key block of S and dP live at a time
     }
@@ -783,11 +818,18 @@ __global__ __launch_bounds__(NT, 2) void attn_bwd_dq_kernel(const BwdArgs a) {
         dp = mfma32(*(const bf16x8*)&Vs[buf][off], greg[s], dp);
       }
       float dsv[16], dmv[16];
+      auto probs = [&](auto poly) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kp = n0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-        const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
-        dsv[j] = bwd_prob<SM>(a, sc[j], l2, bias, dmv[j]);
+        for (int j = 0; j < 16; ++j) {
+          const int kp = n0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          const float bias = SM == SM_ALIBI ? slope2 * (float)(kp - q) : 0.f;
+          dsv[j] = bwd_prob<SM, decltype(poly)::value>(a, sc[j], l2, bias, dmv[j]);
+        }
+      };
+      if (bwd_poly_tile<SM, 1>(a, &sc)) {
+        probs(std::true_type{});
+      } else {
+        probs(std::false_type{});
       }
       if (!full) {
         i32x4 kd4[4];  // document ids of this lane's keys, four per 16-byte LDS read

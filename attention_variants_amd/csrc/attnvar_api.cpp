@@ -51,6 +51,24 @@ int diff_launch(av::DiffArgs& a, const void* q, const void* k, const void* v, vo
 
 }  // namespace
 
+// tanh(x) ~= x (c0 + c1 x^2) on |x| <= 0.25, max relative error 6.4e-5: the
+// minimax (equal-ripple) fit of tanh(x)/x there.  In the exponent that is at
+// most 6.4e-5 * cap*log2(e) * tanh(0.25) <= 7.5e-4 for every cap with
+// 2 * cap * log2(e) <= 96, below a third of the 2^-9 rounding of the bf16
+// probabilities.  Scores of N(0,1)-scaled attention stay inside the range
+// except on a few tiles per thousand, which take the exact form.  In raw
+// units (x = k raw, k = scale / cap) and log2 units:
+// cap*log2(e) * tanh(k raw) = raw * sum_i (cap*log2(e) * c_i * k^(2i+1)) raw^(2i).
+static void softcap_cubic(double scale, double cap, float (&poly)[2], float& lim) {
+  constexpr double c[2] = {0.9999366663950144, -0.3251848147732782};
+  constexpr double kPolyX = 0.25;
+  const double k = scale / cap;
+  const double cap2 = cap * kLog2e;
+  double kp = k;
+  for (int i = 0; i < 2; ++i, kp *= k * k) poly[i] = (float)(cap2 * c[i] * kp);
+  lim = (float)(kPolyX / k);
+}
+
 extern "C" {
 
 int av_abi_version(void) { return AV_ABI_VERSION; }
@@ -169,23 +187,7 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   // softcapped scores lie in [-cap, cap]: with the reference at +cap every
   // exponential is in [2^(-2 cap log2 e), 1], far from fp32 underflow when <= 96
   a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
-  if (a.fixed_ref) {
-    // tanh(x) ~= x (c0 + c1 x^2) on |x| <= 0.25, max relative error 6.4e-5:
-    // the minimax (equal-ripple) fit of tanh(x)/x there.  In the exponent that
-    // is at most 6.4e-5 * cap*log2(e) * tanh(0.25) <= 7.5e-4 for every
-    // fixed-reference cap, below a third of the 2^-9 rounding of the bf16
-    // probabilities.  Scores of N(0,1)-scaled attention stay inside the range
-    // except on a few tiles per thousand, which take the exact form.  In raw
-    // units (x = k raw, k = scale / cap) and log2 units:
-    // cap*log2(e) * tanh(k raw) = raw * sum_i (cap*log2(e) * c_i * k^(2i+1)) raw^(2i).
-    constexpr double c[2] = {0.9999366663950144, -0.3251848147732782};
-    constexpr double kPolyX = 0.25;
-    const double k = scale / (double)var->softcap;
-    const double cap2 = (double)var->softcap * kLog2e;
-    double kp = k;
-    for (int i = 0; i < 2; ++i, kp *= k * k) a.sc_poly[i] = (float)(cap2 * c[i] * kp);
-    a.sc_poly_lim = (float)(kPolyX / k);
-  }
+  if (a.fixed_ref) softcap_cubic(scale, var->softcap, a.sc_poly, a.sc_poly_lim);
   if (tbias) {
     a.bias = var->bias;
     a.bias_bs = var->bias_batch_stride;
@@ -436,6 +438,10 @@ int attn_bwd(const av_variant* var, const void* q, const void* k, const void* v,
   a.c = (float)(scale * kLog2e);
   a.softcap = var->score_mod == AV_SCORE_SOFTCAP ? var->softcap : 1.f;
   a.sc_k = (float)(2.0 * scale * kLog2e / a.softcap);
+  a.sc_inv_cap2 = (float)(1.0 / (a.softcap * kLog2e));
+  a.sc_poly_lim = -1.f;
+  if (var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0)
+    softcap_cubic(scale, var->softcap, a.sc_poly, a.sc_poly_lim);
   a.alibi_max_bias = var->alibi_max_bias;
   a.window = var->window;
   a.prefix = var->prefix_len;

@@ -153,6 +153,12 @@ struct BwdArgs {
   int prefix;         // MK_PREFIX
   const int* doc;     // MK_DOC: [B, S] document ids
   const int* doc_order;  // MK_DOC, optional: heaviest-first order of the 128-row tiles (attn_doc_order)
+  // softcap on a tile whose raw scores all satisfy |raw| <= sc_poly_lim (the
+  // forward's cubic): cap*log2(e)*tanh(scale*raw/cap) = raw*(sc_poly[0] +
+  // sc_poly[1]*raw^2); sc_poly_lim < 0 keeps every tile on the exact form
+  float sc_poly[2];
+  float sc_poly_lim;
+  float sc_inv_cap2;  // 1 / (cap*log2(e))
 };
 hipError_t launch_attn_bwd(const BwdArgs& a, int score_mod, int mask, hipStream_t stream);
 // Zero `bytes` (a multiple of 16, 16-byte aligned) with a kernel (no memset

@@ -38,18 +38,19 @@ def _mask_kw(mask, B, S):
     return kw, dev_kw
 
 
-def _run(av, B, Hq, Hkv, S, score_mod, mask, seed=(21, 22, 23), dseed=24):
+def _run(av, B, Hq, Hkv, S, score_mod, mask, seed=(21, 22, 23), dseed=24, qmul=1.0):
+    """qmul (a power of two, exact in bf16) scales q on both sides."""
     D = 64
     x = wi.attention_inputs(B, Hq, Hkv, S, S, D, seeds=seed)
     g = wi.normal_bf16(dseed, (B, Hq, S, D), 1.0)
-    q, k, v, dout = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
+    q, k, v, dout = to_dev(x["q"]) * qmul, to_dev(x["k"]), to_dev(x["v"]), to_dev(g)
     okw, dkw = _mask_kw(mask, B, S)
     kw = dict(score_mod=score_mod, mask=mask, softcap=20.0)
     out, lse = av.attn_fwd(q, k, v, return_lse=True, **kw, **dkw)
     dq, dk, dv = av.attn_bwd(q, k, v, dout, lse, **kw, **dkw)
     torch.cuda.synchronize()
-    rq, rk, rv = oracle.attention_backward(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(g), **kw, **okw)
-    what = f"bwd {score_mod}/{mask} B{B} Hq{Hq} Hkv{Hkv} S{S}"
+    rq, rk, rv = oracle.attention_backward(f64(x["q"]) * qmul, f64(x["k"]), f64(x["v"]), f64(g), **kw, **okw)
+    what = f"bwd {score_mod}/{mask} B{B} Hq{Hq} Hkv{Hkv} S{S} qmul {qmul}"
     e = [assert_close(dq.float().cpu().numpy(), rq, what + " dq"),
          assert_close(dk.float().cpu().numpy(), rk, what + " dk"),
          assert_close(dv.float().cpu().numpy(), rv, what + " dv")]
@@ -66,6 +67,17 @@ def test_bwd_parity(gpu_lib, score_mod, mask):
 def test_bwd_longer(gpu_lib):
     _run(gpu_lib, 2, 8, 2, 1024, "softcap", "causal")
     _run(gpu_lib, 1, 4, 4, 777, "none", "none")
+
+
+@pytest.mark.parametrize("qmul", [2.0, 4.0])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_bwd_softcap_tiles_outside_the_cubic(gpu_lib, qmul, mask):
+    """Softcap (cap 20, scale 1/8) keeps the cubic for tiles whose raw scores stay
+    within |q.k| <= 0.25 cap / scale = 40 and takes the exact tanh form on the
+    others.  With q doubled (raw score sd 16) the two forms alternate from tile
+    to tile; with q times 4 (sd 32) almost every tile is exact."""
+    _run(gpu_lib, 1, 4, 2, 640, "softcap", mask, qmul=qmul)
+    _run(gpu_lib, 2, 2, 2, 129, "softcap", mask, qmul=qmul)
 
 
 @pytest.mark.parametrize("mask", ["sliding_window", "prefix_lm", "document"])
