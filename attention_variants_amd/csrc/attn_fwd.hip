@@ -231,6 +231,18 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK, ONE>())) void attn_fwd_ke
         qreg[qb][s] = *(const bf16x8*)&QOs[(qi[qb] - q0) * KP + s * 16 + hh * 8];
     __syncthreads();  // the key loop reuses these bytes
   }
+  // Fixed-reference softcap without lse: the key loop's S holds x = beta * raw
+  // (q scaled once, rounded to bf16; that rounding moves the log-sum-exp by
+  // about 1.5e-3, so calls that ask for lse keep the unscaled q)
+  constexpr bool kScaledQ = SM == SM_SOFTCAP_FIXED && !EXACT;
+  if constexpr (kScaledQ) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qreg[qb][s][e] = (bf16)((float)qreg[qb][s][e] * a.sc_x[1]);
+  }
 
   f32x16 o[QB][NDB];
 #pragma unroll
@@ -273,27 +285,32 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK, ONE>())) void attn_fwd_ke
                              kBias ? (uint32_t)a.Sq * a.Skv * 2 : 0u);
   // softcap in log2 units: cap*log2e*tanh(raw*scale/cap) = cap2 - 2*cap2 / (1 + 2^(raw*sc_k))
   // = cap2 - 1 / fma(E, invK, invK) with E = 2^(raw*sc_k), invK = 1/(2*cap2): one exp2,
-  // one fma, one rcp; with the fixed reference the kernel keeps t - cap2
+  // one fma, one rcp.  The fixed-reference form keeps t itself (reference 0:
+  // every exponential lies in [2^-cap2, 2^cap2]), in x = beta * raw without lse
   const float cap2 = a.softcap * kLog2e;
-  const float sc_k = 2.f * a.scale * kLog2e / a.softcap;
+  const float sc_k = 2.f * a.scale * kLog2e / a.softcap / (kScaledQ ? a.sc_x[1] : 1.f);
   const float invK = 0.5f / cap2;
   auto softcap_t = [&](float raw) {
     const float r = rcp_fast(fmaf(exp2_fast(raw * sc_k), invK, invK));
-    return SM == SM_SOFTCAP_FIXED ? -r : cap2 - r;
+    return cap2 - r;
   };
   if constexpr (SM == SM_SOFTCAP_FIXED) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = cap2;  // the scores hold t - m_ref already
+    for (int qb = 0; qb < QB; ++qb) st[qb].m_ref = 0.f;  // the scores hold t - m_ref already
   }
-  // Fixed-reference softcap on a tile whose raw scores all lie in
-  // |raw * scale / cap| <= 0.25: cap*tanh is an odd cubic there
-  // (tanh(x) = x (c0 + c1 x^2) within 6.4e-5 relative), so t - cap2 costs
-  // one multiply and two FMAs instead of exp2 + fma + rcp.
-  auto softcap_poly = [&](float raw) {
-    const float w = raw * raw;
-    const float p = fmaf(w, a.sc_poly[1], a.sc_poly[0]);
-    return fmaf(raw, p, -cap2);
+  // Fixed-reference softcap on a tile whose scores all lie in |raw * scale /
+  // cap| <= 0.25: cap*tanh is an odd cubic there (tanh(x) = x (c0 + c1 x^2)
+  // within 6.4e-5 relative), t = raw (p0 + p1 raw^2); with q scaled by beta,
+  // beta^3 = -p1, it is t = x (A - x^2): one FMA and one multiply instead of
+  // exp2 + fma + rcp.
+  auto softcap_poly = [&](float x) {
+    if constexpr (kScaledQ) {
+      return x * fmaf(-x, x, a.sc_x[0]);
+    } else {
+      return x * fmaf(x * x, a.sc_poly[1], a.sc_poly[0]);
+    }
   };
+  const float sc_lim = kScaledQ ? a.sc_x_lim : a.sc_poly_lim;
 
   i32x4 kr[NCH], vr[NCH];
   i32x4 br[kBiasLds ? BCH : 1];
@@ -453,7 +470,7 @@ __global__ __launch_bounds__(NT, (min_waves<D, SM, MK, ONE>())) void attn_fwd_ke
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
           for (int j = 0; j < 16; ++j) s[qb][kb][j] = softcap_poly(s[qb][kb][j]);
-      if (any_lane(amax > a.sc_poly_lim)) {
+      if (any_lane(amax > sc_lim)) {
         qk(s, buf, bq);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)

@@ -187,7 +187,15 @@ int attn_fwd(const av_variant* var, const void* q, const void* k, const void* v,
   // softcapped scores lie in [-cap, cap]: with the reference at +cap every
   // exponential is in [2^(-2 cap log2 e), 1], far from fp32 underflow when <= 96
   a.fixed_ref = var->score_mod == AV_SCORE_SOFTCAP && 2.0 * var->softcap * kLog2e <= 96.0;
-  if (a.fixed_ref) softcap_cubic(scale, var->softcap, a.sc_poly, a.sc_poly_lim);
+  if (a.fixed_ref) {
+    // raw (p0 + p1 raw^2) with p1 < 0 is x (A - x^2) in x = beta raw, beta^3 =
+    // -p1, A = p0 / beta: without lse the kernel scales q by beta
+    softcap_cubic(scale, var->softcap, a.sc_poly, a.sc_poly_lim);
+    const double beta = cbrt(-(double)a.sc_poly[1]);
+    a.sc_x[0] = (float)(a.sc_poly[0] / beta);
+    a.sc_x[1] = (float)beta;
+    a.sc_x_lim = (float)(a.sc_poly_lim * beta);
+  }
   if (tbias) {
     a.bias = var->bias;
     a.bias_bs = var->bias_batch_stride;

@@ -44,10 +44,14 @@ struct AttnArgs {
   int prefix;
   int fixed_ref;     // softcap with 2 * cap * log2(e) <= 96: exponent reference fixed at the cap
   long long bias_bs, bias_hs;  // bias element strides of batch and head (0 = shared)
-  // fixed-reference softcap: t - cap*log2(e) = fma(raw, P(raw^2), -cap*log2(e)) with the
-  // linear P below, valid while |raw| <= sc_poly_lim (raw = unscaled q.k)
+  // fixed-reference softcap: t = cap*log2(e)*tanh(scale*raw/cap) = raw * P(raw^2) with
+  // the linear P below, valid while |raw| <= sc_poly_lim (raw = unscaled q.k); without
+  // lse the kernel scales q by beta = sc_x[1] and in x = beta * raw t = x * (sc_x[0] - x^2),
+  // valid while |x| <= sc_x_lim
   float sc_poly[2];
   float sc_poly_lim;
+  float sc_x[2];
+  float sc_x_lim;
   int one_block;     // causal / PrefixLM rows run one 32-row block per wave (attn_one_block)
 };
 
